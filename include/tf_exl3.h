@@ -1,0 +1,154 @@
+/*
+ * tf_exl3.h - C ABI of the MI355X (gfx950) EXL3 decode-row projection.
+ *
+ * The projection is the one described on the TensorFold pull request
+ * "hip exl3: the input rotation and trellis linear for decode rows, under the
+ * kernel contract", section "What this changes":
+ *
+ *   rot_in:  z = RN16( H128(x * suh) * s )      per 128-wide block of each row
+ *   linear:  y = cast( svh * ( H128(z . W) * s ) ) per 128-wide block of outputs
+ *
+ * where H128 is the unscaled 128-point Walsh-Hadamard transform, s is the fp32
+ * value of 1/sqrt(128) (multiplied, not divided), and W is an in_dim x out_dim
+ * weight matrix stored as a K-bit shift-register trellis over 16 x 16 tiles and
+ * decoded in registers through a multiplicative-hash codebook. The stream format
+ * (bit order, window, value order, tile order, codebook constants) is fixed in
+ * the comments of tf_exl3_linear below.
+ *
+ * Conventions for every call:
+ *  - Data pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, frees nothing and keeps no mutable global state; calls
+ *    are thread-safe.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Launches are
+ *    asynchronous; the caller synchronizes.
+ *  - Arguments are checked on the host before anything is launched. On a
+ *    refusal (negative status) nothing is launched and nothing is written.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef TF_EXL3_H
+#define TF_EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of rows and outputs. */
+enum {
+  TF_DT_F32 = 0,  /* IEEE binary32 */
+  TF_DT_F16 = 1,  /* IEEE binary16 */
+  TF_DT_BF16 = 2  /* bfloat16 (top half of binary32) */
+};
+
+/* Status codes. */
+enum {
+  TF_OK = 0,
+  TF_E_BITS = -1,   /* bits not in {2, 3, 4, 5, 6, 8} */
+  TF_E_SHAPE = -2,  /* a dimension < 128, not a multiple of 128, or a stream >= 4 GiB */
+  TF_E_ROWS = -3,   /* rows < 0 */
+  TF_E_DTYPE = -4,  /* element type outside the table above */
+  TF_E_NULL = -5,   /* a required pointer is NULL */
+  TF_E_ALIGN = -6,  /* trellis or z not 16-byte aligned, or a row buffer not element-aligned */
+  TF_E_ALIAS = -7,  /* an output overlaps an input */
+  TF_E_WAVES = -8,  /* waves not in {0, 4, 8} */
+  TF_E_LAUNCH = -9  /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * rot_in: the input rotation ("What this changes", first item; the rounding
+ * rules are the ones the page's "Checks on this head" section tests).
+ *
+ * For each row r and each 128-block b of in_dim:
+ *   p_i = RN32(f32(x[r][128b+i]) * f32(suh[128b+i]))
+ *   butterflies over p in stages h = 1, 2, 4, ..., 64: (p_i, p_i+h) <- (RN32(p_i + p_i+h),
+ *     RN32(p_i - p_i+h)) for every i with (i & h) == 0
+ *   z[r][128b+i] = RN16(RN32(p_i * s)),  s = RN32(1/sqrt(128)) = 0x3DB504F3
+ * Two roundings at the end (fp32 product, then fp16), never one fused rounding.
+ * RN is round-to-nearest-even; fp16 subnormals are kept; overflow gives inf.
+ *
+ *  x      [rows][in_dim], row-major, element type x_dtype (TF_DT_F32/F16/BF16)
+ *  suh    [in_dim] fp16 input signs/scales
+ *  z      [rows][in_dim] fp16 output, row-major, 16-byte aligned, must not overlap x
+ *  rows   >= 0 (0 launches nothing)
+ *  in_dim multiple of 128
+ */
+int tf_exl3_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z,
+                   int rows, int in_dim, void* stream);
+
+/*
+ * linear: the trellis linear ("What this changes", second item).
+ *
+ *   acc[r][n] = sum over k of z[r][k] * W[k][n], fp16 products summed in fp32
+ *   y[r][128c+j] = cast_y( RN32( RN32(H128(acc[r][128c..])_j * s) * f32(svh[128c+j]) ) )
+ *
+ * A row's sum is a chain of v_dot2_f32_f16 over (k, k+1) pairs in a fixed
+ * order that depends only on (in_dim, waves), never on how many rows share the
+ * launch: a row's output bits are the same alone, in any window of rows and in
+ * any pass. Rows are processed 16 per pass; rows > 16 run ceil(rows/16) passes.
+ *
+ * Stream format (tile layout). W is in_dim x out_dim; tile (kt, nt) holds
+ * W[16kt .. 16kt+15][16nt .. 16nt+15] and is 8*bits little-endian uint32 words
+ * starting at word (kt * out_dim/16 + nt) * 8*bits. Bit i of a tile is
+ * (word[i >> 5] >> (i & 31)) & 1. Value j = 0..255 of a tile sits at k = j % 16,
+ * n = j / 16, and its state is the 16-bit window of tile bits j*bits .. j*bits+15
+ * (bit t of the state = tile bit (j*bits + t) mod 256*bits; the window wraps).
+ * Codebook: x = (state * 0x9E3779) mod 2^32; h = sum of the four bytes of x;
+ * w = RN16((1024 + h) * A + B) in one fused multiply-add, A = fp16 0x1EEE,
+ * B = fp16 0xC931.
+ *
+ *  bits     2, 3, 4, 5, 6 or 8
+ *  rows     >= 0 (0 launches nothing)
+ *  in_dim, out_dim  multiples of 128; in_dim*out_dim*bits/8 < 2^32
+ *  z        [rows][in_dim] fp16 (rot_in's output), 16-byte aligned
+ *  trellis  tf_exl3_trellis_bytes(bits, in_dim, out_dim) bytes, 16-byte aligned
+ *  svh      [out_dim] fp16 output signs/scales
+ *  y        [rows][out_dim], element type y_dtype; must not overlap z, trellis or svh
+ *  waves    waves per 128-column block: 0 = planner's choice (8 if out_dim >= 8192,
+ *           else 4), or 4, or 8. The wave count fixes the summation order.
+ */
+int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                   const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                   int waves, void* stream);
+
+/* Launch plan the linear would use (host only; no GPU needed). */
+typedef struct {
+  int width_index;    /* position of bits in {2, 3, 4, 5, 6, 8} */
+  int waves;          /* waves per block */
+  int threads;        /* threads per block (64 * waves) */
+  int grid_x;         /* blocks per pass = out_dim / 128 */
+  int passes;         /* ceil(rows / 16) */
+  int rows_last_pass; /* rows in the last pass (1..16), 0 when rows == 0 */
+  int rows_kernel;    /* row capacity of the kernel variant used for a full pass */
+  int lds_bytes;      /* LDS per block of a full pass */
+} tf_exl3_plan;
+
+/* Fills *out with the plan for these arguments, or returns the refusal the linear
+ * would return (TF_E_BITS, TF_E_SHAPE, TF_E_ROWS, TF_E_WAVES, TF_E_NULL if out is NULL). */
+int tf_exl3_linear_plan(int bits, int rows, int in_dim, int out_dim, int waves,
+                        tf_exl3_plan* out);
+
+/* Bytes of a trellis stream: in_dim * out_dim * bits / 8 (0 for a refused shape). */
+size_t tf_exl3_trellis_bytes(int bits, int in_dim, int out_dim);
+
+/* Static text for a status code (never NULL). */
+const char* tf_exl3_status_string(int status);
+
+/*
+ * Test entry points. They run the same device decode functions as the linear.
+ *
+ * debug_decode_states: w[i] = codebook(states[i]) as fp16 bits, i < n.
+ *   states, w: device arrays of n uint16; n >= 0.
+ * debug_decode_tiles: W[k][n] (fp16 bits, [in_dim][out_dim] row-major) decoded from
+ *   a tile-layout stream through the linear's own load, window and codebook path.
+ */
+int tf_exl3_debug_decode_states(const uint16_t* states, uint16_t* w, int n, void* stream);
+int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
+                               uint16_t* w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TF_EXL3_H */

@@ -1,0 +1,180 @@
+"""ctypes binding of libtf_exl3.so (the C ABI declared in include/tf_exl3.h).
+
+Marshalling only: torch tensors supply device memory and the current HIP
+stream; every step of the projection runs in the library's kernels. If the
+library is missing, loading fails loudly: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libtf_exl3.so"
+HEADER = PKG.parent / "include" / "tf_exl3.h"
+
+TF_DT_F32, TF_DT_F16, TF_DT_BF16 = 0, 1, 2
+TF_OK = 0
+STATUS = {
+    0: "TF_OK", -1: "TF_E_BITS", -2: "TF_E_SHAPE", -3: "TF_E_ROWS", -4: "TF_E_DTYPE",
+    -5: "TF_E_NULL", -6: "TF_E_ALIGN", -7: "TF_E_ALIAS", -8: "TF_E_WAVES", -9: "TF_E_LAUNCH",
+}
+
+
+class Exl3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("width_index", ctypes.c_int),
+        ("waves", ctypes.c_int),
+        ("threads", ctypes.c_int),
+        ("grid_x", ctypes.c_int),
+        ("passes", ctypes.c_int),
+        ("rows_last_pass", ctypes.c_int),
+        ("rows_kernel", ctypes.c_int),
+        ("lds_bytes", ctypes.c_int),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "tf_exl3_rot_in": (_I, [_P, _I, _P, _P, _I, _I, _P]),
+    "tf_exl3_linear": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
+    "tf_exl3_trellis_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "tf_exl3_status_string": (ctypes.c_char_p, [_I]),
+    "tf_exl3_debug_decode_states": (_I, [_P, _P, _I, _P]),
+    "tf_exl3_debug_decode_tiles": (_I, [_I, _I, _I, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load(path: str | os.PathLike | None = None) -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise ImportError(
+            f"{p} is missing: build it with __graft_entry__.build() or "
+            "python trellis_quantized_linear_tf_amd/_build.py (hipcc, gfx950)"
+        )
+    lib = ctypes.CDLL(str(p))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/tf_exl3.h declares."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-zA-Z_][\w\s\*]*?\b(tf_exl3_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return load().tf_exl3_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != TF_OK:
+        raise Exl3Error(status, status_string(status))
+
+
+def trellis_bytes(bits: int, in_dim: int, out_dim: int) -> int:
+    return int(load().tf_exl3_trellis_bytes(bits, in_dim, out_dim))
+
+
+def linear_plan(bits: int, rows: int, in_dim: int, out_dim: int, waves: int = 0) -> dict:
+    p = Plan()
+    _check(load().tf_exl3_linear_plan(bits, rows, in_dim, out_dim, waves, ctypes.byref(p)))
+    return p.as_dict()
+
+
+# ---------------------------------------------------------------------------
+# Tensor entry points (torch supplies memory and the stream).
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dt_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return TF_DT_F32
+    if dtype == torch.float16:
+        return TF_DT_F16
+    if dtype == torch.bfloat16:
+        return TF_DT_BF16
+    raise ValueError(f"unsupported element type {dtype}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def rot_in(x, suh, z=None):
+    """z[rows][in_dim] fp16 = rot_in(x, suh); x is fp32/fp16/bf16 [rows][in_dim], suh fp16 [in_dim]."""
+    torch = _torch()
+    rows, in_dim = x.shape
+    if z is None:
+        z = torch.empty((rows, in_dim), dtype=torch.float16, device=x.device)
+    _check(load().tf_exl3_rot_in(_ptr(x), _dt_code(x.dtype), _ptr(suh), _ptr(z), rows, in_dim, _stream(x)))
+    return z
+
+
+def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0):
+    """y[rows][out_dim] = the trellis linear of fp16 z [rows][in_dim] (trellis: uint8/int32 stream)."""
+    torch = _torch()
+    rows, in_dim = z.shape
+    if y is None:
+        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
+    _check(load().tf_exl3_linear(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y),
+                                 _dt_code(y.dtype), waves, _stream(z)))
+    return y
+
+
+def debug_decode_states(states):
+    """fp16 weights (as int16 bits) of uint16 states given as an int16/int32 tensor of 16-bit values."""
+    torch = _torch()
+    s = states.to(torch.int16) if states.dtype != torch.int16 else states
+    w = torch.empty_like(s)
+    _check(load().tf_exl3_debug_decode_states(_ptr(s), _ptr(w), s.numel(), _stream(s)))
+    return w
+
+
+def debug_decode_tiles(trellis, bits: int, in_dim: int, out_dim: int):
+    """W[in_dim][out_dim] as fp16 decoded by the linear's own decode path."""
+    torch = _torch()
+    w = torch.empty((in_dim, out_dim), dtype=torch.float16, device=trellis.device)
+    _check(load().tf_exl3_debug_decode_tiles(bits, in_dim, out_dim, _ptr(trellis), _ptr(w), _stream(trellis)))
+    return w

@@ -1,0 +1,164 @@
+// Device building blocks of the EXL3 decode-row projection for gfx950 (wave64).
+//
+// The projection is the one the TensorFold pull request "hip exl3: the input
+// rotation and trellis linear for decode rows" describes in "What this
+// changes"; the stream format and rounding rules are stated in tf_exl3.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tf_exl3 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 128;               // rotation block and output strip width
+constexpr int kRowsPerPass = 16;
+constexpr uint32_t kHashMul = 0x9E3779u;  // < 2^24, so v_mul_u32_u24 is exact
+constexpr uint32_t kScaleBits = 0x3DB504F3u;  // RN32(1/sqrt(128))
+constexpr uint32_t kCbScale = 0x1EEEu;    // fp16 A
+constexpr uint32_t kCbBias = 0xC931u;     // fp16 B
+
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Keeps the compiler from fusing an fp32 value into its consumer (a multiply
+// followed by an fp16 convert would otherwise become one v_fma_mix rounding).
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  const _Float16 h = (_Float16)v;  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; a NaN stays a quiet NaN of the same sign.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t u = f32_to_bits(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Codebook: two 16-bit states -> two packed fp16 weights.
+//   x = state * 0x9E3779 (low 32 bits); h = byte sum of x;
+//   w = fma(1024 + h, A, B) in fp16, one rounding.
+// 1024 + h is the fp16 whose bits are 0x6400 + h (h <= 1020 keeps it in
+// [1024, 2048)), so the byte sums land directly in packed fp16 form: v_sad_u8
+// adds the first sum to 0x64006400 and v_sad_hi_u8 adds the second sum shifted
+// into the top half; one v_pk_fma_f16 then finishes both values.
+__device__ __forceinline__ half2_t decode_pair(uint32_t s0, uint32_t s1) {
+  const uint32_t x0 = __umul24(s0, kHashMul);
+  const uint32_t x1 = __umul24(s1, kHashMul);
+  uint32_t t = __builtin_amdgcn_sad_u8(x0, 0u, 0x64006400u);
+  t = __builtin_amdgcn_sad_hi_u8(x1, 0u, t);
+  const half2_t v = __builtin_bit_cast(half2_t, t);
+  const half2_t a = __builtin_bit_cast(half2_t, kCbScale * 0x10001u);
+  const half2_t b = __builtin_bit_cast(half2_t, kCbBias * 0x10001u);
+  return __builtin_elementwise_fma(v, a, b);
+}
+
+// 16-bit window starting at bit i*BITS of the little-endian word array w[]
+// (i is a constant after unrolling, so the word index and shift fold away).
+template <int BITS>
+__device__ __forceinline__ uint32_t window_at(const uint32_t* w, int i) {
+  const int o = i * BITS;
+  const int d = o >> 5;
+  const int sh = o & 31;
+  const uint32_t v = (sh <= 16) ? (w[d] >> sh) : __builtin_amdgcn_alignbit(w[d + 1], w[d], sh);
+  return v & 0xFFFFu;
+}
+
+// Funnel shift: bits [sh, sh + 32) of the 64-bit value hi:lo. Kept opaque so
+// the compiler does not narrow it when only one half of the result is used.
+template <int SH>
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo) {
+  uint32_t r;
+  asm("v_alignbit_b32 %0, %1, %2, %3" : "=v"(r) : "v"(hi), "v"(lo), "i"(SH));
+  return r;
+}
+
+// The 32 states of a lane's share (see decode_lane). When BITS divides 16 the
+// window at offset o + 16 is the top half of the funnel shift that gives the
+// window at o, so one shift serves two states; the 16-bit halves then reach
+// v_mul_u32_u24 through its WORD_0 / WORD_1 operand selects at no cost.
+template <int BITS, int I = 0>
+__device__ __forceinline__ void lane_states(const uint32_t (&w)[BITS + 1], uint32_t (&st)[32]) {
+  if constexpr (I < 32) {
+    constexpr int o = I * BITS;
+    constexpr int d = o >> 5;
+    constexpr int sh = o & 31;
+    if constexpr (16 % BITS == 0) {
+      if constexpr (sh < 16) {
+        uint32_t t;
+        if constexpr (sh == 0) {
+          t = w[d];
+        } else {
+          t = funnel<sh>(w[d + 1], w[d]);
+        }
+        st[I] = t & 0xFFFFu;
+        st[I + 16 / BITS] = t >> 16;
+      }
+    } else {
+      st[I] = window_at<BITS>(w, I);
+    }
+    lane_states<BITS, I + 1>(w, st);
+  }
+}
+
+// A lane's share of one tile row of a 128-column strip. The strip's tile row is
+// 8 tiles of 32*BITS bytes, contiguous; lane = 8t + q holds the BITS dwords at
+// bits 32*BITS*q .. of tile t, which are tile values 32q .. 32q+31 = strip
+// columns 2*lane and 2*lane+1, 16 k values each. w[BITS] is the next lane's
+// first dword (within the tile, q = 7 wrapping to q = 0): it completes the last
+// windows, which reach at most 16 - BITS bits past the lane's own bits.
+// Output: wp[c][p] = packed (W[2p][2*lane+c], W[2p+1][2*lane+c]) of the tile row.
+template <int BITS>
+__device__ __forceinline__ void decode_lane(const uint32_t (&w)[BITS + 1], half2_t (&wp)[2][8]) {
+  uint32_t st[32];
+  lane_states<BITS>(w, st);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) wp[c][p] = decode_pair(st[16 * c + 2 * p], st[16 * c + 2 * p + 1]);
+  }
+}
+
+// Lane that holds the dword following this lane's share inside the same tile.
+__device__ __forceinline__ int next_lane_in_tile(int lane) { return (lane & ~7) | ((lane + 1) & 7); }
+
+// ---------------------------------------------------------------------------
+// 128-point butterflies on one wave: element e of the block lives in lane e % 64,
+// register e / 64 (v0 holds e = lane, v1 holds e = lane + 64). Stages run
+// h = 1, 2, ..., 64; in stage h the pair (i, i+h), i & h == 0, becomes
+// (a + b, a - b) rounded to fp32. Stages 1..32 pair lanes lane ^ h; a lane in
+// the upper half of a pair computes fma(v, -1, partner) = partner - v exactly as
+// a subtraction would (v * -1 is exact, one rounding follows). Stage 64 pairs
+// v0 with v1 inside the lane.
+__device__ __forceinline__ void fwht128_wave(float& v0, float& v1) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int h = 1; h < kWave; h <<= 1) {
+    const float sgn = (lane & h) ? -1.0f : 1.0f;
+    const float p0 = __shfl_xor(v0, h);
+    const float p1 = __shfl_xor(v1, h);
+    v0 = __builtin_fmaf(v0, sgn, p0);
+    v1 = __builtin_fmaf(v1, sgn, p1);
+  }
+  const float a = v0;
+  const float b = v1;
+  v0 = a + b;
+  v1 = a - b;
+}
+
+}  // namespace tf_exl3

@@ -1,0 +1,30 @@
+// Internal launch interface between the C ABI (exl3_abi.cpp) and the kernels.
+// Arguments reaching these functions have already been checked by the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace tf_exl3 {
+
+// Row capacity of the linear kernel variant that serves `rows` (1..16) rows.
+inline int rows_bucket(int rows) {
+  return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
+}
+
+// LDS bytes of one linear block: the waves' partial sums [waves][rows][128] fp32.
+inline int linear_lds_bytes(int waves, int rows_cap) { return waves * rows_cap * 128 * 4; }
+
+hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,
+                         int in_dim, hipStream_t stream);
+
+hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                         hipStream_t stream);
+
+hipError_t launch_decode_states(const uint16_t* states, uint16_t* w, int n, hipStream_t stream);
+
+hipError_t launch_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
+                               uint16_t* w, hipStream_t stream);
+
+}  // namespace tf_exl3

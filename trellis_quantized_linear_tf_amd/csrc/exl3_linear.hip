@@ -1,0 +1,297 @@
+// The trellis linear for 1..16 decode rows per pass.
+//
+// TensorFold pull request "hip exl3: the input rotation and trellis linear for
+// decode rows", "What this changes": a lane decodes its 16 x 16 tile values with
+// one fp16 fma each; a row's sums are v_dot2_f32_f16 chains in a fixed order, so
+// a row's bits do not depend on the rows sharing its launch; the waves' partial
+// sums, the output rotation and svh finish the block; no K split, no bias.
+//
+// Work layout on gfx950:
+//  - one workgroup per (128-column strip, pass of up to 16 rows);
+//  - the strip's tile row kt is 8 contiguous tiles = 256*BITS bytes, read by one
+//    wave as one coalesced load (BITS dwords per lane); lane l owns strip
+//    columns 2l and 2l+1;
+//  - wave w takes tile rows kt = w, w + WAVES, ... (in_dim/16 is a multiple of
+//    8, so every wave gets the same count), with a register ring of PF tile rows
+//    in flight;
+//  - z pairs are wave-uniform and come in through scalar loads, feeding
+//    v_dot2_f32_f16 as the SGPR operand;
+//  - the partial sums go through LDS and are added in wave order 0..WAVES-1;
+//    one wave per row then runs the 128-point butterflies, the scale and svh.
+// A row's chain is: for each of its wave's tile rows in ascending kt, the pairs
+// p = 0..7 in ascending k; it is the same in every row-capacity variant.
+#include "exl3_device.hpp"
+#include "exl3_launch.hpp"
+#include "tf_exl3.h"
+
+namespace tf_exl3 {
+
+// Tile rows in flight per wave: about 4 KiB of stream per wave.
+template <int BITS>
+constexpr int prefetch_depth() {
+  return BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 4 ? 4 : BITS == 8 ? 2 : 3;
+}
+
+// A lane's share of a tile row plus the first dword of the next lane's share
+// (`nb_off` dwords away, wrapping inside the tile), which completes the last
+// windows. The extra dword lies in cache lines the wave loads anyway.
+template <int BITS>
+__device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint32_t* __restrict__ src,
+                                           int nb_off) {
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) dst[i] = src[i];
+  dst[BITS] = src[nb_off];
+}
+
+__device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, size_t i, float v) {
+  if (y_dtype == TF_DT_F32) {
+    static_cast<float*>(y)[i] = v;
+  } else if (y_dtype == TF_DT_F16) {
+    static_cast<uint16_t*>(y)[i] = f32_to_f16_bits(v);
+  } else {
+    static_cast<uint16_t*>(y)[i] = f32_to_bf16_bits(v);
+  }
+}
+
+// One tile row of the strip for one wave: decode 32 weights per lane and chain
+// the dot products of every row.
+template <int BITS, int WAVES, int NR>
+__device__ __forceinline__ void tile_row_step(const uint32_t (&w)[BITS + 1], int i,
+                                              const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
+  half2_t wp[2][8];
+  decode_lane<BITS>(w, wp);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t* zp = zrow[r] + i * (WAVES * 8);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const half2_t zz = __builtin_bit_cast(half2_t, zp[p]);
+      acc[r][0] = __builtin_amdgcn_fdot2(zz, wp[0][p], acc[r][0], false);
+      acc[r][1] = __builtin_amdgcn_fdot2(zz, wp[1][p], acc[r][1], false);
+    }
+  }
+}
+
+template <int BITS, int WAVES, int NR>
+__global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __restrict__ z,
+                                                              const uint32_t* __restrict__ trellis,
+                                                              const uint16_t* __restrict__ svh,
+                                                              void* __restrict__ y, int y_dtype,
+                                                              int rows, int in_dim, int out_dim) {
+  constexpr int PF = prefetch_depth<BITS>();
+  __shared__ float partial[WAVES * NR * kBlock];
+
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int strip = blockIdx.x;
+  const int r0 = blockIdx.y * kRowsPerPass;
+  const int nr = min(NR, rows - r0);
+  const int iters = in_dim / 16 / WAVES;
+
+  // Stream words of one tile row across the whole matrix, and this lane's share
+  // of tile row kt = wave in this strip.
+  const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
+  const uint32_t* __restrict__ tp =
+      trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS + (size_t)lane * BITS;
+  const size_t step_words = (size_t)WAVES * row_words;
+  const int nb_off = (next_lane_in_tile(lane) - lane) * BITS;
+
+  // Row r of this pass reads z as dword pairs; padded rows (r >= nr) repeat the
+  // last real row and are never stored.
+  const uint32_t* zrow_m[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int rr = r0 + (r < nr ? r : nr - 1);
+    zrow_m[r] = reinterpret_cast<const uint32_t*>(z + (size_t)rr * in_dim) + wave * 8;
+  }
+  const uint32_t* const(&zrow)[NR] = zrow_m;
+
+  float acc[NR][2];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r][0] = acc[r][1] = 0.0f;
+
+  // Step i (0 <= i < iters) is tile row kt = wave + i * WAVES. Loads are issued
+  // PF steps ahead; addresses past the last step are clamped to it, so the ring
+  // needs no branches and the wait counts stay exact.
+  auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
+  uint32_t ring[PF][BITS + 1];
+#pragma unroll
+  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), nb_off);
+
+  int it = 0;
+  for (; it + PF <= iters; it += PF) {
+#pragma unroll
+    for (int d = 0; d < PF; ++d) {
+      uint32_t w[BITS + 1];
+#pragma unroll
+      for (int b = 0; b <= BITS; ++b) w[b] = ring[d][b];
+      load_share<BITS>(ring[d], share(it + d + PF), nb_off);
+      tile_row_step<BITS, WAVES, NR>(w, it + d, zrow, acc);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < PF; ++d) {
+    if (it + d < iters) {
+      tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
+    }
+  }
+
+  // Cross-wave sums in wave order, then the output rotation, scale and svh.
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float2 v;
+    v.x = acc[r][0];
+    v.y = acc[r][1];
+    *reinterpret_cast<float2*>(&partial[(wave * NR + r) * kBlock + 2 * lane]) = v;
+  }
+  __syncthreads();
+
+  const float s = bits_to_f32(kScaleBits);
+  const int col = strip * kBlock + lane;
+  const float g0 = f16_bits_to_f32(svh[col]);
+  const float g1 = f16_bits_to_f32(svh[col + 64]);
+  for (int r = wave; r < nr; r += WAVES) {
+    float v0 = partial[r * kBlock + lane];
+    float v1 = partial[r * kBlock + lane + 64];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      v0 = v0 + partial[(w * NR + r) * kBlock + lane];
+      v1 = v1 + partial[(w * NR + r) * kBlock + lane + 64];
+    }
+    fwht128_wave(v0, v1);
+    v0 = opaque(v0 * s);
+    v1 = opaque(v1 * s);
+    v0 = opaque(v0 * g0);
+    v1 = opaque(v1 * g1);
+    const size_t o = (size_t)(r0 + r) * out_dim + col;
+    store_out(y, y_dtype, o, v0);
+    store_out(y, y_dtype, o + 64, v1);
+  }
+}
+
+template <int BITS, int WAVES>
+static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
+                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                            hipStream_t stream) {
+  const int full = rows / kRowsPerPass;
+  const int rest = rows % kRowsPerPass;
+  const dim3 block(kWave * WAVES);
+  if (full > 0) {
+    hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 16>), dim3(out_dim / kBlock, full), block, 0,
+                       stream, z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim, out_dim);
+  }
+  if (rest > 0) {
+    const size_t off = (size_t)full * kRowsPerPass;
+    const uint16_t* zr = z + off * in_dim;
+    void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
+                                      : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
+    const dim3 grid(out_dim / kBlock, 1);
+    switch (rows_bucket(rest)) {
+      case 1:
+        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 1>), grid, block, 0, stream, zr, trellis, svh,
+                           yr, y_dtype, rest, in_dim, out_dim);
+        break;
+      case 2:
+        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 2>), grid, block, 0, stream, zr, trellis, svh,
+                           yr, y_dtype, rest, in_dim, out_dim);
+        break;
+      case 4:
+        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 4>), grid, block, 0, stream, zr, trellis, svh,
+                           yr, y_dtype, rest, in_dim, out_dim);
+        break;
+      case 8:
+        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 8>), grid, block, 0, stream, zr, trellis, svh,
+                           yr, y_dtype, rest, in_dim, out_dim);
+        break;
+      default:
+        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 16>), grid, block, 0, stream, zr, trellis,
+                           svh, yr, y_dtype, rest, in_dim, out_dim);
+        break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                           const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                           hipStream_t stream) {
+  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+}
+
+hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                         hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  switch (bits) {
+    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Test kernels on the same device decode path.
+
+__global__ __launch_bounds__(256) void decode_states_kernel(const uint16_t* __restrict__ states,
+                                                             uint16_t* __restrict__ w, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t s = states[i];
+  w[i] = (uint16_t)(__builtin_bit_cast(uint32_t, decode_pair(s, s)) & 0xFFFFu);
+}
+
+// One wave per (strip, tile row): the linear's share load, neighbour exchange and
+// decode_lane, then the 32 weights of each lane are written out as W[k][n].
+template <int BITS>
+__global__ __launch_bounds__(kWave) void decode_tiles_kernel(const uint32_t* __restrict__ trellis,
+                                                              uint16_t* __restrict__ w_out,
+                                                              int out_dim) {
+  const int lane = __lane_id();
+  const int strip = blockIdx.x;
+  const int kt = blockIdx.y;
+  const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
+  const uint32_t* tp = trellis + (size_t)kt * row_words + (size_t)strip * 64 * BITS + (size_t)lane * BITS;
+  uint32_t w[BITS + 1];
+  load_share<BITS>(w, tp, (next_lane_in_tile(lane) - lane) * BITS);
+  half2_t wp[2][8];
+  decode_lane<BITS>(w, wp);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const size_t n = (size_t)strip * kBlock + 2 * lane + c;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      // Halves through the packed dword (bit-casting a vector element directly
+      // is lowered as element 0 by this compiler).
+      const uint32_t u = __builtin_bit_cast(uint32_t, wp[c][p]);
+      w_out[(size_t)(16 * kt + 2 * p) * out_dim + n] = (uint16_t)(u & 0xFFFFu);
+      w_out[(size_t)(16 * kt + 2 * p + 1) * out_dim + n] = (uint16_t)(u >> 16);
+    }
+  }
+}
+
+hipError_t launch_decode_states(const uint16_t* states, uint16_t* w, int n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_states_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, states, w, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
+                               uint16_t* w, hipStream_t stream) {
+  const dim3 grid(out_dim / kBlock, in_dim / 16);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(decode_tiles_kernel<2>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+    case 3: hipLaunchKernelGGL(decode_tiles_kernel<3>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+    case 4: hipLaunchKernelGGL(decode_tiles_kernel<4>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+    case 5: hipLaunchKernelGGL(decode_tiles_kernel<5>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+    case 6: hipLaunchKernelGGL(decode_tiles_kernel<6>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+    default: hipLaunchKernelGGL(decode_tiles_kernel<8>, grid, dim3(kWave), 0, stream, trellis, w, out_dim); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tf_exl3

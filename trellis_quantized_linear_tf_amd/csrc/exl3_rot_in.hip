@@ -1,0 +1,77 @@
+// rot_in: z = RN16(RN32(H128(RN32(x * suh)) * s)) per 128-wide block of each row.
+//
+// TensorFold pull request "hip exl3: the input rotation and trellis linear for
+// decode rows": "What this changes" (x times suh, rotated by 128, rounded to
+// fp16 once: the fp32 product, the butterflies, then the scale) and "Checks on
+// this head" (multiply by the fp32 scale rather than divide; keep the fp32
+// product and the fp16 conversion as two roundings).
+//
+// One wave per 128-block: lane l holds elements l and l + 64 (fwht128_wave).
+// The work is a few hundred KiB per call, so the kernel is latency-bound; four
+// waves per workgroup keep the grid small.
+#include "exl3_device.hpp"
+#include "exl3_launch.hpp"
+#include "tf_exl3.h"
+
+namespace tf_exl3 {
+
+constexpr int kRotWaves = 4;
+
+template <int XDT>
+__device__ __forceinline__ float load_in(const void* __restrict__ x, size_t i) {
+  if constexpr (XDT == TF_DT_F32) {
+    return static_cast<const float*>(x)[i];
+  } else if constexpr (XDT == TF_DT_F16) {
+    return f16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+  } else {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+  }
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kWave* kRotWaves) void rot_in_kernel(const void* __restrict__ x,
+                                                                  const uint16_t* __restrict__ suh,
+                                                                  uint16_t* __restrict__ z,
+                                                                  int blocks_per_row,
+                                                                  long long n_blocks) {
+  const int lane = __lane_id();
+  const long long blk = (long long)blockIdx.x * kRotWaves + (threadIdx.x >> 6);
+  if (blk >= n_blocks) return;
+  const int kb = (int)(blk % blocks_per_row);
+  const size_t base = (size_t)blk * kBlock;  // row * in_dim + kb * 128
+  const int col = kb * kBlock + lane;
+
+  const float p0 = load_in<XDT>(x, base + lane) * f16_bits_to_f32(suh[col]);
+  const float p1 = load_in<XDT>(x, base + lane + 64) * f16_bits_to_f32(suh[col + 64]);
+  float v0 = opaque(p0);
+  float v1 = opaque(p1);
+  fwht128_wave(v0, v1);
+  const float s = bits_to_f32(kScaleBits);
+  v0 = opaque(v0 * s);
+  v1 = opaque(v1 * s);
+  z[base + lane] = f32_to_f16_bits(v0);
+  z[base + lane + 64] = f32_to_f16_bits(v1);
+}
+
+hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,
+                         int in_dim, hipStream_t stream) {
+  const int bpr = in_dim / kBlock;
+  const long long n_blocks = (long long)rows * bpr;
+  if (n_blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_blocks + kRotWaves - 1) / kRotWaves));
+  const dim3 block(kWave * kRotWaves);
+  switch (x_dtype) {
+    case TF_DT_F32:
+      hipLaunchKernelGGL(rot_in_kernel<TF_DT_F32>, grid, block, 0, stream, x, suh, z, bpr, n_blocks);
+      break;
+    case TF_DT_F16:
+      hipLaunchKernelGGL(rot_in_kernel<TF_DT_F16>, grid, block, 0, stream, x, suh, z, bpr, n_blocks);
+      break;
+    default:
+      hipLaunchKernelGGL(rot_in_kernel<TF_DT_BF16>, grid, block, 0, stream, x, suh, z, bpr, n_blocks);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tf_exl3
