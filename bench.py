@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the EXL3 decode-row projection on one MI355X.
+
+Workload: the LM head, 5120 -> 129,280 at 4 bits, fp16 input rows ~N(0, 0.5),
++-1 suh/svh, fp32 logits. One step is rot_in on the rows followed by the trellis
+linear: the whole path, on inputs already resident in HBM. The headline value is
+one row per step (a decode token); a second timed region runs 16 rows per step.
+
+The weight stream is 331 MB; steps alternate between two copies of it (662 MB,
+more than the 256 MB Infinity Cache and the L2s together), so no step reads a
+stream that the previous step left in a cache.
+
+Prints one JSON line (see the fields at the end of main()).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "weight-stream GB/s and rows/s per MI355X (LM head 5120→129280, 4-bit, 1–16 rows)"
+HBM_PEAK_GBPS = 8000.0
+BITS, IN_DIM, OUT_DIM = 4, 5120, 129280
+WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
+CPU_SAMPLE_STRIPS = 128
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
+KERNEL_SOURCES = ["exl3_device.hpp", "exl3_linear.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "trellis_quantized_linear_tf_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(rows: int) -> dict:
+    """Bytes the linear must move per launch: the stream, z, y, svh."""
+    stream = IN_DIM * OUT_DIM * BITS // 8
+    z = rows * IN_DIM * 2
+    y = rows * OUT_DIM * 4
+    svh = OUT_DIM * 2
+    return {"stream": stream, "total": stream + z + y + svh}
+
+
+def load_traffic(rows: int):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    per_rows = rec.get("per_launch_bytes", {}).get(str(rows))
+    return per_rows
+
+
+def make_inputs(torch, dev, rows: int, copies: int):
+    import numpy as np
+
+    import synth
+
+    stream = synth.trellis_words(synth.seed_for(WORKLOAD_ID, synth.STREAM_TRELLIS), BITS, IN_DIM, OUT_DIM)
+    x = synth.rows(synth.seed_for(WORKLOAD_ID, synth.STREAM_ROWS), rows, IN_DIM, "f16", 0.5)
+    suh = synth.signs(synth.seed_for(WORKLOAD_ID, synth.STREAM_SUH), IN_DIM)
+    svh = synth.signs(synth.seed_for(WORKLOAD_ID, synth.STREAM_SVH), OUT_DIM)
+    t_host = torch.from_numpy(stream.view(np.int32))
+    trellis = [t_host.to(dev) for _ in range(copies)]
+    xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
+    suh_t = torch.from_numpy(suh.view(np.int16)).to(dev).view(torch.float16)
+    svh_t = torch.from_numpy(svh.view(np.int16)).to(dev).view(torch.float16)
+    return trellis, xt, suh_t, svh_t, (stream, x, suh, svh)
+
+
+def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps; HIP events around every linear launch."""
+    rows = xt.shape[0]
+    z = torch.empty((rows, IN_DIM), dtype=torch.float16, device=xt.device)
+    y = torch.empty((rows, OUT_DIM), dtype=torch.float32, device=xt.device)
+    copies = len(trellis)
+    for i in range(warmup):
+        tq.rot_in(xt, suh_t, z)
+        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        tq.rot_in(xt, suh_t, z)
+        ev[i][0].record(stream)
+        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    lin_ms = [a.elapsed_time(b) for a, b in ev]
+    return total_ms, lin_ms, wall, y
+
+
+def cpu_baseline(host_inputs, rows: int) -> dict:
+    """The oracle (rot_in fp32 steps + float64 linear) on a bounded sample of strips."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import linear as lin
+    from oracle import rotation as rot
+
+    stream, x, suh, svh = host_inputs
+    strips = np.arange(CPU_SAMPLE_STRIPS)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        z = rot.rot_in(x[:rows], "f16", suh)
+        lin.linear_f64(z, stream, BITS, IN_DIM, OUT_DIM, svh, strips=strips)
+        dt = time.perf_counter() - t0
+    sample_stream_bytes = IN_DIM * 128 * CPU_SAMPLE_STRIPS * BITS // 8
+    return {
+        "value": round(sample_stream_bytes / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rows} row, {CPU_SAMPLE_STRIPS} of 1010 strips (5120 x 16384 weights), "
+                  f"rot_in + float64 linear, {dt:.1f} s",
+        "rows_per_s": round(rows * CPU_SAMPLE_STRIPS / 1010 / dt, 6),
+    }
+
+
+def calibrate_copy(torch, dev, steps: int) -> None:
+    """A plain 1 GiB device copy, for scaling the HBM byte counters."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", type=int, default=1, help="rows of the headline region")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the projection shards by "
+              "output columns with no exchange, so N GPUs each run this kernel on N-th of the strips).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import trellis_quantized_linear_tf_amd as tq
+    from trellis_quantized_linear_tf_amd import _lib
+
+    if not _lib.LIB_PATH.exists():
+        from trellis_quantized_linear_tf_amd._build import build
+
+        build()
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, args.steps)
+        return 0
+
+    rows = args.rows
+    trellis, xt, suh_t, svh_t, host = make_inputs(torch, dev, 16, copies=2)
+    total_ms, lin_ms, wall, y = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t,
+                                           args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    lin_avg_ms = sum(lin_ms) / len(lin_ms)
+    ab = algorithmic_bytes(rows)
+    stream_gbps = ab["stream"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["total"] / (lin_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(rows)
+
+    extra = {}
+    if not args.no_r16 and rows != 16:
+        t16, l16, _, _ = time_steps(torch, tq, trellis, xt, suh_t, svh_t, args.steps, args.warmup)
+        ab16 = algorithmic_bytes(16)
+        l16_avg = sum(l16) / len(l16)
+        extra["rows16"] = {
+            "ms_per_step": round(t16 / args.steps, 5),
+            "value": round(ab16["stream"] / (t16 / args.steps * 1e-3) / 1e9, 2),
+            "rows_per_s": round(16 / (t16 / args.steps * 1e-3), 1),
+            "linear_ms": round(l16_avg, 5),
+            "hbm_frac": round(ab16["total"] / (l16_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+
+    cpu = None if args.no_cpu else cpu_baseline(host, rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(stream_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"LM head {IN_DIM}->{OUT_DIM}, {BITS}-bit trellis, {rows} fp16 row(s) ~N(0,0.5), "
+                        "+-1 suh/svh, fp32 out; step = rot_in + linear",
+            "in_dim": IN_DIM, "out_dim": OUT_DIM, "bits": BITS, "rows": rows,
+            "waves": tq.linear_plan(BITS, rows, IN_DIM, OUT_DIM)["waves"],
+            "stream_copies": len(trellis),
+        },
+        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "tf_exl3::linear_kernel<4, 8, 1>",
+            "kernel_ms": round(lin_avg_ms, 5),
+            "bytes_per_launch": ab["total"],
+        },
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+        **extra,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
