@@ -141,7 +141,7 @@ def calibrate_copy(torch, dev, steps: int) -> None:
     a = torch.ones(n, dtype=torch.int32, device=dev)
     b = torch.empty_like(a)
     for _ in range(steps):
-        b.copy_(a)
+        torch.mul(a, 1, out=b)  # an elementwise kernel: reads 1 GiB, writes 1 GiB
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": steps}))
 

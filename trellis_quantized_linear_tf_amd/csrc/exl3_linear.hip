@@ -32,15 +32,17 @@ constexpr int prefetch_depth() {
   return BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 4 ? 4 : BITS == 8 ? 2 : 3;
 }
 
-// A lane's share of a tile row plus the first dword of the next lane's share
-// (`nb_off` dwords away, wrapping inside the tile), which completes the last
-// windows. The extra dword lies in cache lines the wave loads anyway.
+// A lane's share of a tile row plus the first dword of the next lane's share,
+// which completes the last windows (it lies in cache lines the wave loads
+// anyway). `p` is the wave-uniform start of the strip's tile row (an SGPR
+// pair), `off` the lane's dword offset and `nb` the next lane's (wrapping
+// inside the tile), so the loads take the scalar-base + vector-offset form.
 template <int BITS>
-__device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint32_t* __restrict__ src,
-                                           int nb_off) {
+__device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint32_t* __restrict__ p, int off,
+                                           int nb) {
 #pragma unroll
-  for (int i = 0; i < BITS; ++i) dst[i] = src[i];
-  dst[BITS] = src[nb_off];
+  for (int i = 0; i < BITS; ++i) dst[i] = p[off + i];
+  dst[BITS] = p[nb];
 }
 
 __device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, size_t i, float v) {
@@ -91,10 +93,10 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   // Stream words of one tile row across the whole matrix, and this lane's share
   // of tile row kt = wave in this strip.
   const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
-  const uint32_t* __restrict__ tp =
-      trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS + (size_t)lane * BITS;
+  const uint32_t* __restrict__ tp = trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS;
   const size_t step_words = (size_t)WAVES * row_words;
-  const int nb_off = (next_lane_in_tile(lane) - lane) * BITS;
+  const int off = lane * BITS;
+  const int nb = next_lane_in_tile(lane) * BITS;
 
   // Row r of this pass reads z as dword pairs; padded rows (r >= nr) repeat the
   // last real row and are never stored.
@@ -110,30 +112,28 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r][0] = acc[r][1] = 0.0f;
 
-  // Step i (0 <= i < iters) is tile row kt = wave + i * WAVES. Loads are issued
-  // PF steps ahead; addresses past the last step are clamped to it, so the ring
-  // needs no branches and the wait counts stay exact.
+  // Step i (0 <= i < iters) is tile row kt = wave + i * WAVES. A ring of PF + 1
+  // slots keeps PF steps in flight: step i decodes slot i % (PF + 1) while the
+  // load for step i + PF goes to the slot step i - 1 has just freed. Addresses
+  // past the last step are clamped to it, so the ring needs no branches and the
+  // wait counts stay exact.
+  constexpr int RING = PF + 1;
   auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
-  uint32_t ring[PF][BITS + 1];
+  uint32_t ring[RING][BITS + 1];
 #pragma unroll
-  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), nb_off);
+  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
 
   int it = 0;
-  for (; it + PF <= iters; it += PF) {
+  for (; it + RING <= iters; it += RING) {
 #pragma unroll
-    for (int d = 0; d < PF; ++d) {
-      uint32_t w[BITS + 1];
-#pragma unroll
-      for (int b = 0; b <= BITS; ++b) w[b] = ring[d][b];
-      load_share<BITS>(ring[d], share(it + d + PF), nb_off);
-      tile_row_step<BITS, WAVES, NR>(w, it + d, zrow, acc);
+    for (int d = 0; d < RING; ++d) {
+      load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off, nb);
+      tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
     }
   }
 #pragma unroll
-  for (int d = 0; d < PF; ++d) {
-    if (it + d < iters) {
-      tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
-    }
+  for (int d = 0; d < RING; ++d) {
+    if (it + d < iters) tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
   }
 
   // Cross-wave sums in wave order, then the output rotation, scale and svh.
@@ -255,9 +255,9 @@ __global__ __launch_bounds__(kWave) void decode_tiles_kernel(const uint32_t* __r
   const int strip = blockIdx.x;
   const int kt = blockIdx.y;
   const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
-  const uint32_t* tp = trellis + (size_t)kt * row_words + (size_t)strip * 64 * BITS + (size_t)lane * BITS;
+  const uint32_t* tp = trellis + (size_t)kt * row_words + (size_t)strip * 64 * BITS;
   uint32_t w[BITS + 1];
-  load_share<BITS>(w, tp, (next_lane_in_tile(lane) - lane) * BITS);
+  load_share<BITS>(w, tp, lane * BITS, next_lane_in_tile(lane) * BITS);
   half2_t wp[2][8];
   decode_lane<BITS>(w, wp);
 #pragma unroll
