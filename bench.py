@@ -135,15 +135,81 @@ def cpu_baseline(host_inputs, rows: int) -> dict:
     }
 
 
-def calibrate_copy(torch, dev, steps: int) -> None:
-    """A plain 1 GiB device copy, for scaling the HBM byte counters."""
-    n = 1 << 28
-    a = torch.ones(n, dtype=torch.int32, device=dev)
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(torch, tq, dev, steps: int) -> None:
+    """The library's plain copy kernel on 1 GiB (for scaling the HBM byte counters)."""
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
     b = torch.empty_like(a)
     for _ in range(steps):
-        torch.mul(a, 1, out=b)  # an elementwise kernel: reads 1 GiB, writes 1 GiB
+        tq.calib_copy(a, b)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": steps}))
+    print(json.dumps({"calibration": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "launches": steps}))
+
+
+def read_ceiling(torch, tq, dev, launches: int = 20) -> float:
+    """GB/s of the library's read-only stream kernel over 1 GiB buffers (two, alternating)."""
+    bufs = [torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+    out = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    for i in range(3):
+        tq.calib_stream_read(bufs[i % 2], out)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(launches):
+        tq.calib_stream_read(bufs[i % 2], out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / launches
+    del bufs
+    return COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def _counter_means(directory: Path, kernel_substr: str) -> dict:
+    """Mean per dispatch of each counter for kernels whose name contains kernel_substr."""
+    import csv
+    import glob
+
+    files = glob.glob(str(directory / "**" / "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    vals: dict = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if kernel_substr in row["Kernel_Name"]:
+                vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def ingest_counters(base: Path) -> dict:
+    """Build the traffic record from rocprofv3 --pmc runs under `base`:
+    copy_fetch/, copy_write/ (bench.py --calibrate-copy), r{R}_fetch/, r{R}_write/ (bench.py --rows R)."""
+    copy_fetch = _counter_means(base / "copy_fetch", "copy_kernel")["FETCH_SIZE"]
+    copy_write = _counter_means(base / "copy_write", "copy_kernel")["WRITE_SIZE"]
+    f_read = COPY_BYTES / (copy_fetch * 1024)
+    f_write = COPY_BYTES / (copy_write * 1024)
+    per = {}
+    for rows in (1, 16):
+        d_f, d_w = base / f"r{rows}_fetch", base / f"r{rows}_write"
+        if not d_f.exists():
+            continue
+        name = f"linear_kernel<{BITS}, 8, {rows}>"
+        fetch = _counter_means(d_f, name)["FETCH_SIZE"]
+        write = _counter_means(d_w, name)["WRITE_SIZE"]
+        per[str(rows)] = int(round(fetch * 1024 * f_read + write * 1024 * f_write))
+    rec = {
+        "kernel_source_hash": kernel_source_hash(),
+        "copy_kib_per_launch": {"FETCH_SIZE": copy_fetch, "WRITE_SIZE": copy_write},
+        "scale": {"read": f_read, "write": f_write},
+        "per_launch_bytes": per,
+        "algorithmic_bytes": {r: algorithmic_bytes(int(r))["total"] for r in per},
+    }
+    TRAFFIC_FILE.parent.mkdir(exist_ok=True)
+    TRAFFIC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+    return rec
 
 
 def main() -> int:
@@ -155,7 +221,12 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
+    ap.add_argument("--ingest-counters", metavar="DIR", help="write the traffic record from --pmc runs in DIR")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(Path(args.ingest_counters))))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the projection shards by "
@@ -174,7 +245,7 @@ def main() -> int:
         build()
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
-        calibrate_copy(torch, dev, args.steps)
+        calibrate_copy(torch, tq, dev, args.steps)
         return 0
 
     rows = args.rows
@@ -201,6 +272,7 @@ def main() -> int:
             "hbm_frac": round(ab16["total"] / (l16_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         }
 
+    ceiling = read_ceiling(torch, tq, dev)
     cpu = None if args.no_cpu else cpu_baseline(host, rows)
 
     out = {
@@ -234,6 +306,8 @@ def main() -> int:
             "kernel": "tf_exl3::linear_kernel<4, 8, 1>",
             "kernel_ms": round(lin_avg_ms, 5),
             "bytes_per_launch": ab["total"],
+            "read_ceiling": round(ceiling, 2),
+            "frac_of_read_ceiling": round(achieved / ceiling, 4),
         },
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),

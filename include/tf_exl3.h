@@ -147,6 +147,19 @@ int tf_exl3_debug_decode_states(const uint16_t* states, uint16_t* w, int n, void
 int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
                                uint16_t* w, void* stream);
 
+/*
+ * Calibration entry points for measurement (not part of the projection). Both
+ * move 16 bytes per lane in wave-contiguous 1 KiB runs, the access form of the
+ * linear's weight stream.
+ *
+ * calib_copy: dst[0 .. bytes) = src[0 .. bytes); bytes a multiple of 16, both
+ *   16-byte aligned and disjoint; `blocks` workgroups of 256 threads (>= 1).
+ * calib_stream_read: reads src[0 .. bytes) and writes one XOR word per thread
+ *   to out, which must hold blocks * 256 uint32 and not overlap src.
+ */
+int tf_exl3_calib_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
+int tf_exl3_calib_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     TF_DT_F32,
     Exl3Error,
     debug_decode_states,
+    calib_copy,
+    calib_stream_read,
     debug_decode_tiles,
     header_functions,
     linear,

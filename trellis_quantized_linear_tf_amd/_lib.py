@@ -56,6 +56,8 @@ SIGNATURES = {
     "tf_exl3_status_string": (ctypes.c_char_p, [_I]),
     "tf_exl3_debug_decode_states": (_I, [_P, _P, _I, _P]),
     "tf_exl3_debug_decode_tiles": (_I, [_I, _I, _I, _P, _P, _P]),
+    "tf_exl3_calib_copy": (_I, [_P, _P, ctypes.c_size_t, _I, _P]),
+    "tf_exl3_calib_stream_read": (_I, [_P, ctypes.c_size_t, _P, _I, _P]),
 }
 
 _lib = None
@@ -178,3 +180,17 @@ def debug_decode_tiles(trellis, bits: int, in_dim: int, out_dim: int):
     w = torch.empty((in_dim, out_dim), dtype=torch.float16, device=trellis.device)
     _check(load().tf_exl3_debug_decode_tiles(bits, in_dim, out_dim, _ptr(trellis), _ptr(w), _stream(trellis)))
     return w
+
+
+def calib_copy(src, dst, blocks: int = 2048):
+    """dst <- src byte for byte (both contiguous device tensors of equal byte size)."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes
+    _check(load().tf_exl3_calib_copy(_ptr(src), _ptr(dst), nbytes, blocks, _stream(src)))
+
+
+def calib_stream_read(src, out):
+    """Reads all of src; out is an int32 tensor of blocks * 256 entries."""
+    nbytes = src.numel() * src.element_size()
+    blocks = out.numel() // 256
+    _check(load().tf_exl3_calib_stream_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(src)))

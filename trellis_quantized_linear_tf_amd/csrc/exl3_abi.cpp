@@ -159,4 +159,25 @@ int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 
+int tf_exl3_calib_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+  if (bytes % 16 != 0) return TF_E_SHAPE;
+  if (blocks < 1) return TF_E_SHAPE;
+  if (bytes == 0) return TF_OK;
+  if (src == nullptr || dst == nullptr) return TF_E_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return TF_E_ALIGN;
+  if (overlap(src, bytes, dst, bytes)) return TF_E_ALIAS;
+  const hipError_t e = tf_exl3::launch_copy(src, dst, bytes, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
+int tf_exl3_calib_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream) {
+  if (bytes % 16 != 0) return TF_E_SHAPE;
+  if (blocks < 1) return TF_E_SHAPE;
+  if (src == nullptr || out == nullptr) return TF_E_NULL;
+  if (!aligned(src, 16) || !aligned(out, 4)) return TF_E_ALIGN;
+  if (overlap(src, bytes, out, (size_t)blocks * 256 * 4)) return TF_E_ALIAS;
+  const hipError_t e = tf_exl3::launch_stream_read(src, bytes, out, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
 }  // extern "C"

@@ -27,4 +27,8 @@ hipError_t launch_decode_states(const uint16_t* states, uint16_t* w, int n, hipS
 hipError_t launch_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
                                uint16_t* w, hipStream_t stream);
 
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream);
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks, hipStream_t stream);
+
 }  // namespace tf_exl3

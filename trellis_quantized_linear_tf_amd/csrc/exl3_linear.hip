@@ -34,15 +34,15 @@ constexpr int prefetch_depth() {
 
 // A lane's share of a tile row plus the first dword of the next lane's share,
 // which completes the last windows (it lies in cache lines the wave loads
-// anyway). `p` is the wave-uniform start of the strip's tile row (an SGPR
+// anyway). The stream is read once, so the loads are nontemporal. `p` is the wave-uniform start of the strip's tile row (an SGPR
 // pair), `off` the lane's dword offset and `nb` the next lane's (wrapping
 // inside the tile), so the loads take the scalar-base + vector-offset form.
 template <int BITS>
 __device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint32_t* __restrict__ p, int off,
                                            int nb) {
 #pragma unroll
-  for (int i = 0; i < BITS; ++i) dst[i] = p[off + i];
-  dst[BITS] = p[nb];
+  for (int i = 0; i < BITS; ++i) dst[i] = __builtin_nontemporal_load(p + off + i);
+  dst[BITS] = __builtin_nontemporal_load(p + nb);
 }
 
 __device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, size_t i, float v) {
