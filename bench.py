@@ -31,6 +31,7 @@ HBM_PEAK_GBPS = 8000.0
 BITS, IN_DIM, OUT_DIM = 4, 5120, 129280
 WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
 CPU_SAMPLE_STRIPS = 128
+WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
 KERNEL_SOURCES = ["exl3_device.hpp", "exl3_linear.hip"]
 
@@ -79,15 +80,21 @@ def make_inputs(torch, dev, rows: int, copies: int):
     return trellis, xt, suh_t, svh_t, (stream, x, suh, svh)
 
 
-def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int):
+def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, engine: str = "dot2"):
     """Warm up, then time exactly `steps` steps; HIP events around every linear launch."""
     rows = xt.shape[0]
     z = torch.empty((rows, IN_DIM), dtype=torch.float16, device=xt.device)
     y = torch.empty((rows, OUT_DIM), dtype=torch.float32, device=xt.device)
     copies = len(trellis)
-    for i in range(warmup):
+    # At least `warmup` steps and at least WARMUP_S seconds, so clocks settle first.
+    t_start = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_start < WARMUP_S:
         tq.rot_in(xt, suh_t, z)
-        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -98,7 +105,7 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int):
     for i in range(steps):
         tq.rot_in(xt, suh_t, z)
         ev[i][0].record(stream)
-        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
         ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -106,6 +113,11 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int):
     total_ms = t0.elapsed_time(t1)
     lin_ms = [a.elapsed_time(b) for a, b in ev]
     return total_ms, lin_ms, wall, y
+
+
+def _percentiles(v):
+    s = sorted(v)
+    return [s[int(q * (len(s) - 1))] for q in (0.1, 0.5, 0.9)]
 
 
 def cpu_baseline(host_inputs, rows: int) -> dict:
@@ -218,6 +230,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", type=int, default=1, help="rows of the headline region")
+    ap.add_argument("--engine", choices=["dot2", "mfma"], default="dot2",
+                    help="linear engine of the headline: v_dot2 chains or matrix cores")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
@@ -250,8 +264,9 @@ def main() -> int:
 
     rows = args.rows
     trellis, xt, suh_t, svh_t, host = make_inputs(torch, dev, 16, copies=2)
+    engine = args.engine
     total_ms, lin_ms, wall, y = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t,
-                                           args.steps, args.warmup)
+                                           args.steps, args.warmup, engine)
     ms_per_step = total_ms / args.steps
     lin_avg_ms = sum(lin_ms) / len(lin_ms)
     ab = algorithmic_bytes(rows)
@@ -260,17 +275,24 @@ def main() -> int:
     traffic = load_traffic(rows)
 
     extra = {}
-    if not args.no_r16 and rows != 16:
-        t16, l16, _, _ = time_steps(torch, tq, trellis, xt, suh_t, svh_t, args.steps, args.warmup)
-        ab16 = algorithmic_bytes(16)
-        l16_avg = sum(l16) / len(l16)
-        extra["rows16"] = {
-            "ms_per_step": round(t16 / args.steps, 5),
-            "value": round(ab16["stream"] / (t16 / args.steps * 1e-3) / 1e9, 2),
-            "rows_per_s": round(16 / (t16 / args.steps * 1e-3), 1),
-            "linear_ms": round(l16_avg, 5),
-            "hbm_frac": round(ab16["total"] / (l16_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        }
+    if not args.no_r16:
+        # Both engines at 1 and 16 rows, same inputs and protocol (the headline is one of them).
+        table = {}
+        for eng in ("dot2", "mfma"):
+            for r in (1, 16):
+                t, l, _, _ = time_steps(torch, tq, trellis, xt[:r].contiguous(), suh_t, svh_t, args.steps,
+                                        args.warmup, eng)
+                abr = algorithmic_bytes(r)
+                l_avg = sum(l) / len(l)
+                table[f"{eng}_rows{r}"] = {
+                    "ms_per_step": round(t / args.steps, 5),
+                    "value": round(abr["stream"] / (t / args.steps * 1e-3) / 1e9, 2),
+                    "rows_per_s": round(r / (t / args.steps * 1e-3), 1),
+                    "linear_ms": round(l_avg, 5),
+                    "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
+                    "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                }
+        extra["engines"] = table
 
     ceiling = read_ceiling(torch, tq, dev)
     cpu = None if args.no_cpu else cpu_baseline(host, rows)
@@ -293,6 +315,7 @@ def main() -> int:
                         "+-1 suh/svh, fp32 out; step = rot_in + linear",
             "in_dim": IN_DIM, "out_dim": OUT_DIM, "bits": BITS, "rows": rows,
             "waves": tq.linear_plan(BITS, rows, IN_DIM, OUT_DIM)["waves"],
+            "engine": engine,
             "stream_copies": len(trellis),
         },
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
@@ -303,8 +326,10 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "tf_exl3::linear_kernel<4, 8, 1>",
+            "kernel": (f"tf_exl3::linear_kernel<{BITS}, 8, {rows}>" if engine == "dot2"
+                       else f"tf_exl3::linear_mfma_kernel<{BITS}, 8>"),
             "kernel_ms": round(lin_avg_ms, 5),
+            "kernel_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
             "bytes_per_launch": ab["total"],
             "read_ceiling": round(ceiling, 2),
             "frac_of_read_ceiling": round(achieved / ceiling, 4),

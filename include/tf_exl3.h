@@ -112,6 +112,20 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
                    const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                    int waves, void* stream);
 
+/*
+ * linear_mfma: the same projection with the same arguments, refusals, stream
+ * format and finish, but the sums over k run on the matrix cores
+ * (v_mfma_f32_32x32x16_f16) instead of v_dot2 chains, so the vector ALUs only
+ * decode and the time no longer grows with the number of rows. Its k order per
+ * output is fixed by (in_dim, waves) and never depends on the rows sharing the
+ * launch; it is a different fixed order from tf_exl3_linear's, so the two agree
+ * to the float64 gate, not bit for bit. (The page's "Known limits" and the
+ * multi-row work it announces are the use; the page's own kernels sum with dot2.)
+ */
+int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                        const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                        int waves, void* stream);
+
 /* Launch plan the linear would use (host only; no GPU needed). */
 typedef struct {
   int width_index;    /* position of bits in {2, 3, 4, 5, 6, 8} */

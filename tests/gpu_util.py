@@ -46,10 +46,10 @@ def rot_in(x, x_dtype, suh):
     return down(z)
 
 
-def linear(z_bits, stream, svh, bits, n, out="f32", waves=0, stream_t=None):
+def linear(z_bits, stream, svh, bits, n, out="f32", waves=0, stream_t=None, engine="dot2"):
     zt = up(z_bits)
     tt = stream_t if stream_t is not None else up(stream)
-    y = tq.linear(zt, tt, up(svh), bits, n, out_dtype=TORCH_DT[out], waves=waves)
+    y = tq.linear(zt, tt, up(svh), bits, n, out_dtype=TORCH_DT[out], waves=waves, engine=engine)
     torch.cuda.synchronize()
     return down(y)
 

@@ -20,6 +20,7 @@ from oracle import rotation as rot
 from tests.gpu_util import TORCH_DT, down, same_bits, say, up
 
 pytestmark = pytest.mark.gpu
+ENGINES = pytest.mark.parametrize("engine", ["dot2", "mfma"])
 
 
 def inputs(workload, bits, k, n, rows, x_dtype, sigma=1.0):
@@ -31,9 +32,9 @@ def inputs(workload, bits, k, n, rows, x_dtype, sigma=1.0):
     return stream, x, suh, svh
 
 
-def run_path(stream_t, x, x_dtype, suh, svh, bits, n, out, waves):
+def run_path(stream_t, x, x_dtype, suh, svh, bits, n, out, waves, engine="dot2"):
     z = tq.rot_in(up(x, x_dtype), up(suh))
-    y = tq.linear(z, stream_t, up(svh), bits, n, out_dtype=TORCH_DT[out], waves=waves)
+    y = tq.linear(z, stream_t, up(svh), bits, n, out_dtype=TORCH_DT[out], waves=waves, engine=engine)
     torch.cuda.synchronize()
     return down(z), y
 
@@ -58,58 +59,63 @@ def check(z_gpu, y_gpu, stream, x, x_dtype, suh, svh, bits, k, n, out, seed):
     return err
 
 
-def test_indexer_wk(gpu):
+@ENGINES
+def test_indexer_wk(gpu, engine):
     bits, k, n = 4, 512, 128
     stream, x, suh, svh = inputs(1, bits, k, n, 1, "f16")
     say("indexer wk 512->128 4-bit, 1 fp16 row, fp32 out, auto waves")
-    z, y = run_path(up(stream), x, "f16", suh, svh, bits, n, "f32", 0)
+    z, y = run_path(up(stream), x, "f16", suh, svh, bits, n, "f32", 0, engine)
     assert tq.linear_plan(bits, 1, k, n)["waves"] == 4
     check(z, y, stream, x, "f16", suh, svh, bits, k, n, "f32", 11)
     y64 = lin.linear_f64(rot.rot_in(x, "f16", suh), stream, bits, k, n, svh)
     assert lin.gate_error(down(y), "f32", y64) <= lin.GATE
 
 
+@ENGINES
 @pytest.mark.parametrize("bits", [3, 4])
-def test_engram_wkv(gpu, bits):
+def test_engram_wkv(gpu, engine, bits):
     k, n = 6144, 25600
     stream, x, suh, svh = inputs(2, bits, k, n, 16, "bf16")
     st = up(stream)
     for rows in (1, 2, 8, 16):
-        say(f"engram wkv 6144->25600 {bits}-bit, {rows} bf16 rows, fp16 out, 4 waves")
-        z, y16 = run_path(st, x[:rows], "bf16", suh, svh, bits, n, "f16", 4)
+        say(f"[{engine}] engram wkv 6144->25600 {bits}-bit, {rows} bf16 rows, fp16 out, 4 waves")
+        z, y16 = run_path(st, x[:rows], "bf16", suh, svh, bits, n, "f16", 4, engine)
         check(z, y16, stream, x[:rows], "bf16", suh, svh, bits, k, n, "f16", 20 + rows)
-        y32 = tq.linear(up(z), st, up(svh), bits, n, out_dtype=torch.float32, waves=4)
+        y32 = tq.linear(up(z), st, up(svh), bits, n, out_dtype=torch.float32, waves=4, engine=engine)
         torch.cuda.synchronize()
         assert same_bits(down(y16), nf.f32_to_output(down(y32), "f16"), "f16")
 
 
 @pytest.mark.parametrize("rows", [1, 16])
-def test_lm_head(gpu, rows):
+@ENGINES
+def test_lm_head(gpu, engine, rows):
     bits, k, n = 4, 5120, 129280
     stream, x, suh, svh = inputs(3, bits, k, n, 16, "f16", 0.5)
-    say(f"lm head 5120->129280 4-bit, {rows} fp16 rows ~N(0,0.5), fp32 out, auto waves")
-    z, y = run_path(up(stream), x[:rows], "f16", suh, svh, bits, n, "f32", 0)
+    say(f"[{engine}] lm head 5120->129280 4-bit, {rows} fp16 rows ~N(0,0.5), fp32 out, auto waves")
+    z, y = run_path(up(stream), x[:rows], "f16", suh, svh, bits, n, "f32", 0, engine)
     assert tq.linear_plan(bits, rows, k, n)["waves"] == 8
     check(z, y, stream, x[:rows], "f16", suh, svh, bits, k, n, "f32", 30 + rows)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
-def test_width_sweep(gpu, bits):
+@ENGINES
+def test_width_sweep(gpu, engine, bits):
     k, n, rows = 6144, 25600, 64
     stream, x, suh, svh = inputs(4, bits, k, n, rows, "f16")
-    say(f"width sweep 6144->25600 {bits}-bit, 64 fp16 rows (4 passes), fp32 out, 8 waves")
-    z, y = run_path(up(stream), x, "f16", suh, svh, bits, n, "f32", 8)
+    say(f"[{engine}] width sweep 6144->25600 {bits}-bit, 64 fp16 rows (4 passes), fp32 out, 8 waves")
+    z, y = run_path(up(stream), x, "f16", suh, svh, bits, n, "f32", 8, engine)
     check(z, y, stream, x, "f16", suh, svh, bits, k, n, "f32", 40 + bits)
 
 
-def test_stress_linear_8bit(gpu):
+@ENGINES
+def test_stress_linear_8bit(gpu, engine):
     bits, k, n = 8, 5120, 129280
     stream, xb, suh, svh = inputs(5, bits, k, n, 64, "bf16")
     xf = synth.heavy_rows(synth.seed_for(5, synth.STREAM_EXTRA), 64, k)
     st = up(stream)
     for x, x_dtype in ((xb, "bf16"), (xf, "f32")):
-        say(f"stress lm head 8-bit, 64 {x_dtype} rows, fp32 out, auto waves")
-        z, y = run_path(st, x, x_dtype, suh, svh, bits, n, "f32", 0)
+        say(f"[{engine}] stress lm head 8-bit, 64 {x_dtype} rows, fp32 out, auto waves")
+        z, y = run_path(st, x, x_dtype, suh, svh, bits, n, "f32", 0, engine)
         check(z, y, stream, x, x_dtype, suh, svh, bits, k, n, "f32", 50)
 
 

@@ -22,6 +22,7 @@ from oracle import trellis as tr
 from tests.gpu_util import down, linear, same_bits, say, up
 
 pytestmark = pytest.mark.gpu
+ENGINES = pytest.mark.parametrize("engine", ["dot2", "mfma"])
 
 
 def make(bits, k, n, rows, seed, sigma=1.0):
@@ -31,109 +32,117 @@ def make(bits, k, n, rows, seed, sigma=1.0):
     return stream, z, svh
 
 
+@ENGINES
 @pytest.mark.parametrize("bits", tr.WIDTHS)
 @pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("k,n,rows", [(128, 128, 1), (256, 384, 3), (512, 1024, 17), (1024, 256, 33)])
-def test_small_shapes_gate(gpu, bits, waves, k, n, rows):
+def test_small_shapes_gate(gpu, engine, bits, waves, k, n, rows):
     stream, z, svh = make(bits, k, n, rows, 1000 * bits + k + rows)
-    say(f"linear bits={bits} waves={waves} k={k} n={n} rows={rows}")
-    y = linear(z, stream, svh, bits, n, "f32", waves)
+    say(f"linear {engine} bits={bits} waves={waves} k={k} n={n} rows={rows}")
+    y = linear(z, stream, svh, bits, n, "f32", waves, engine=engine)
     y64 = lin.linear_f64(z, stream, bits, k, n, svh)
     err = lin.gate_error(y, "f32", y64)
     assert err <= lin.GATE, err
 
 
+@ENGINES
 @pytest.mark.parametrize("out", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [3, 4, 8])
-def test_low_precision_outputs_are_casts(gpu, out, bits):
+def test_low_precision_outputs_are_casts(gpu, engine, out, bits):
     k, n, rows = 512, 768, 5
     stream, z, svh = make(bits, k, n, rows, 77 + bits)
-    say(f"linear bits={bits} out={out}")
-    y32 = linear(z, stream, svh, bits, n, "f32")
-    yt = linear(z, stream, svh, bits, n, out)
+    say(f"linear {engine} bits={bits} out={out}")
+    y32 = linear(z, stream, svh, bits, n, "f32", engine=engine)
+    yt = linear(z, stream, svh, bits, n, out, engine=engine)
     assert same_bits(yt, nf.f32_to_output(y32, out), out)
     assert lin.gate_error(yt, out, lin.linear_f64(z, stream, bits, k, n, svh)) <= lin.GATE
 
 
+@ENGINES
 @pytest.mark.parametrize("bits", tr.WIDTHS)
 @pytest.mark.parametrize("waves", [4, 8])
-def test_identity_rows_give_rotated_weight_rows(gpu, bits, waves):
+def test_identity_rows_give_rotated_weight_rows(gpu, engine, bits, waves):
     k, n = 256, 384
     stream = synth.trellis_words(600 + bits, bits, k, n)
     svh = synth.signs(601, n)
     eye = np.where(np.eye(k, dtype=bool), np.uint16(0x3C00), np.uint16(0)).astype(np.uint16)
-    say(f"identity bits={bits} waves={waves}")
-    y = linear(eye, stream, svh, bits, n, "f32", waves)
+    say(f"identity {engine} bits={bits} waves={waves}")
+    y = linear(eye, stream, svh, bits, n, "f32", waves, engine=engine)
     w = nf.f16_bits_to_f32(tr.unpack(stream, bits, k, n))
     want = lin.finish_f32(w, svh, "f32")
     assert same_bits(y, want), np.argwhere(nf.f32_bits(y) != nf.f32_bits(want))[:5]
 
 
+@ENGINES
 @pytest.mark.parametrize("bits", tr.WIDTHS)
 @pytest.mark.parametrize("waves", [4, 8])
-def test_exact_gate(gpu, bits, waves):
+def test_exact_gate(gpu, engine, bits, waves):
     k, n = 6144, 128
     stream = synth.constant_trellis(bits, k, n, ones=True)
     z = np.full((1, k), 0x6C00, dtype=np.uint16)
     svh = synth.signs(602, n)
-    say(f"exact gate bits={bits} waves={waves}")
-    y = linear(z, stream, svh, bits, n, "f32", waves)[0]
+    say(f"exact gate {engine} bits={bits} waves={waves}")
+    y = linear(z, stream, svh, bits, n, "f32", waves, engine=engine)[0]
     acc = np.full((1, n), 6144 * 2682, dtype=np.float32)
     want = lin.finish_f32(acc, svh, "f32")[0]
     assert same_bits(y, want)
     assert abs(int(nf.f32_bits(y[0])) & 0x7FFFFFFF) == 0x4D31CB0C
 
 
+@ENGINES
 @pytest.mark.parametrize("bits", tr.WIDTHS)
-def test_batch_invariance(gpu, bits):
+def test_batch_invariance(gpu, engine, bits):
     """Each row's bits alone, in windows of 2..24 rows from several first rows, and in
     one 64-row launch (four passes of 16), at 8 waves on 6144 -> 25600."""
     k, n, rows = 6144, 25600, 64
     stream, z, svh = make(bits, k, n, rows, 700 + bits)
-    say(f"batch invariance bits={bits}")
+    say(f"batch invariance {engine} bits={bits}")
     tt = up(stream)
-    full = linear(z, None, svh, bits, n, "f32", 8, stream_t=tt)
+    full = linear(z, None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
     for r in range(rows):
-        alone = linear(z[r : r + 1], None, svh, bits, n, "f32", 8, stream_t=tt)
+        alone = linear(z[r : r + 1], None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
         assert np.array_equal(nf.f32_bits(alone[0]), nf.f32_bits(full[r])), r
     for size in range(2, 25):
         for first in sorted({0, 5, 16 - size // 2, rows - size}):
             if first < 0 or first + size > rows:
                 continue
-            win = linear(z[first : first + size], None, svh, bits, n, "f32", 8, stream_t=tt)
+            win = linear(z[first : first + size], None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
             assert np.array_equal(nf.f32_bits(win), nf.f32_bits(full[first : first + size])), (size, first)
     y64 = lin.linear_f64(z, stream, bits, k, n, svh, strips=[0, 77, 199])
     assert lin.gate_error(full[:, lin.strip_columns([0, 77, 199])], "f32", y64) <= lin.GATE
 
 
-def test_five_runs_byte_identical(gpu):
+@ENGINES
+def test_five_runs_byte_identical(gpu, engine):
     stream, z, svh = make(4, 2048, 8192, 16, 800)
-    say("five runs")
+    say(f"five runs {engine}")
     tt = up(stream)
-    runs = [linear(z, None, svh, 4, 8192, "f32", 0, stream_t=tt) for _ in range(5)]
+    runs = [linear(z, None, svh, 4, 8192, "f32", 0, stream_t=tt, engine=engine) for _ in range(5)]
     assert all(np.array_equal(nf.f32_bits(runs[0]), nf.f32_bits(r)) for r in runs[1:])
 
 
-def test_nonfinite_classes(gpu):
+@ENGINES
+def test_nonfinite_classes(gpu, engine):
     k, n, rows = 512, 512, 4
     stream, z, svh = make(4, k, n, rows, 801)
     z[0, 3] = 0x7C00  # +inf
     z[1, 100] = 0xFC00  # -inf
     z[2, 7] = 0x7E00  # NaN
-    say("non-finite inputs")
-    y = linear(z, stream, svh, 4, n, "f32")
+    say(f"non-finite inputs {engine}")
+    y = linear(z, stream, svh, 4, n, "f32", engine=engine)
     y64 = lin.linear_f64(z, stream, 4, k, n, svh)
     assert np.array_equal(lin.classes(y), lin.classes(y64))
     assert lin.gate_error(y, "f32", y64) <= lin.GATE
     assert np.count_nonzero(lin.classes(y)) >= 3 * n
 
 
-def test_planted_control_rows_one_late(gpu):
+@ENGINES
+def test_planted_control_rows_one_late(gpu, engine):
     bits, k, n, rows = 4, 128, 512, 16
     stream, z, svh = make(bits, k, n, rows + 1, 802)
     say("planted control: z + in_dim")
     zt = up(z)
-    y = tq.linear(zt[1:], up(stream), up(svh), bits, n)
+    y = tq.linear(zt[1:], up(stream), up(svh), bits, n, engine=engine)
     torch.cuda.synchronize()
     y64 = lin.linear_f64(z[:rows], stream, bits, k, n, svh)
     err = lin.gate_error(down(y), "f32", y64)
@@ -141,17 +150,32 @@ def test_planted_control_rows_one_late(gpu):
     assert err > 100 * lin.GATE
 
 
-def test_planted_control_wrong_width(gpu):
+@ENGINES
+def test_planted_control_wrong_width(gpu, engine):
     k, n, rows = 256, 512, 2
     stream, z, svh = make(4, k, n, rows, 803)
     say("planted control: 4-bit stream read as 3-bit")
-    y = linear(z, stream, svh, 3, n)
+    y = linear(z, stream, svh, 3, n, engine=engine)
     y64 = lin.linear_f64(z, stream, 4, k, n, svh)
     assert lin.gate_error(y, "f32", y64) > 100 * lin.GATE
 
 
-def test_zero_rows(gpu):
+@ENGINES
+def test_zero_rows(gpu, engine):
     stream, z, svh = make(4, 128, 128, 0, 804)
-    say("zero rows")
-    y = linear(z, stream, svh, 4, 128)
+    say(f"zero rows {engine}")
+    y = linear(z, stream, svh, 4, 128, engine=engine)
     assert y.shape == (0, 128)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_engines_agree(gpu, bits):
+    """Both engines sit within the gate of float64, hence of each other (not bit for bit:
+    their k orders differ)."""
+    k, n, rows = 1024, 2048, 16
+    stream, z, svh = make(bits, k, n, rows, 805 + bits)
+    say(f"engines agree bits={bits}")
+    a = linear(z, stream, svh, bits, n, engine="dot2")
+    b = linear(z, stream, svh, bits, n, engine="mfma")
+    y64 = lin.linear_f64(z, stream, bits, k, n, svh)
+    assert lin.gate_error(a, "f32", y64) <= lin.GATE and lin.gate_error(b, "f32", y64) <= lin.GATE

@@ -116,10 +116,12 @@ int tf_exl3_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z,
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 
-int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
-                   const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
-  tf_exl3_plan plan;
-  const int st = tf_exl3_linear_plan(bits, rows, in_dim, out_dim, waves, &plan);
+namespace {
+
+// Checks shared by both engines; TF_OK means the launch may proceed (rows > 0).
+int linear_checks(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
+                  const uint16_t* svh, void* y, int y_dtype, int waves, tf_exl3_plan* plan) {
+  const int st = tf_exl3_linear_plan(bits, rows, in_dim, out_dim, waves, plan);
   if (st != TF_OK) return st;
   if (!dtype_ok(y_dtype)) return TF_E_DTYPE;
   if (rows == 0) return TF_OK;
@@ -131,8 +133,28 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
       overlap(y, ny, trellis, (size_t)stream_bytes(bits, in_dim, out_dim)) ||
       overlap(y, ny, svh, (size_t)out_dim * 2))
     return TF_E_ALIAS;
+  return TF_OK;
+}
+
+}  // namespace
+
+int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
+                   const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK || rows == 0) return st;
   const hipError_t e = tf_exl3::launch_linear(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
                                               y_dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
+int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
+                        const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK || rows == 0) return st;
+  const hipError_t e = tf_exl3::launch_linear_mfma(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh,
+                                                   y, y_dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 

@@ -22,6 +22,10 @@ hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim,
                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                          hipStream_t stream);
 
+hipError_t launch_linear_mfma(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                              const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                              hipStream_t stream);
+
 hipError_t launch_decode_states(const uint16_t* states, uint16_t* w, int n, hipStream_t stream);
 
 hipError_t launch_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
