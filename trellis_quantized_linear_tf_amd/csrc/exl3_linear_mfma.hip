@@ -35,11 +35,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit elements
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Tile rows in flight per wave (an odd count, so the ring has an even number of
-// slots and the one-step-ahead A loads can alternate two register sets).
+// Tile rows in flight per wave, and how many steps ahead the A operands load;
+// the ring's PF + 1 slots must be a multiple of the A ring's ZD + 1 slots.
 template <int BITS>
 constexpr int mfma_prefetch() {
-  return BITS == 3 ? 5 : 3;
+  return BITS == 3 || BITS == 5 ? 5 : 3;
+}
+template <int BITS>
+constexpr int mfma_a_ahead() {
+  return mfma_prefetch<BITS>() == 5 ? 2 : 1;
 }
 
 __device__ __forceinline__ half8_t pairs_to_half8(half2_t a, half2_t b, half2_t c, half2_t d) {
@@ -72,14 +76,22 @@ __device__ __forceinline__ void load_a(u32x4 (&za)[2], __amdgpu_buffer_rsrc_t rs
   za[1] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, 0);
 }
 
-// At most 128 registers (arch + accumulators), so four waves share a SIMD.
+// Waves per SIMD the register budget aims at: five (96 registers) where the
+// kernel fits without spilling, else four (128).
+template <int BITS>
+constexpr int mfma_waves_per_simd() {
+  return BITS == 2 || BITS == 4 ? 5 : 4;
+}
+
 template <int BITS, int WAVES>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<BITS>()))) void linear_mfma_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
   constexpr int PF = mfma_prefetch<BITS>();
   constexpr int RING = PF + 1;
-  static_assert(RING % 2 == 0, "A operands alternate two register sets");
+  constexpr int ZD = mfma_a_ahead<BITS>();
+  constexpr int ZR = ZD + 1;
+  static_assert(RING % ZR == 0, "the A ring must line up with the stream ring");
   extern __shared__ float partial[];  // [WAVES][nr][128]
 
   const int lane = __lane_id();
@@ -114,25 +126,26 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   uint32_t ring[RING][BITS + 1];
 #pragma unroll
   for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
-  u32x4 za[2][2];
-  load_a(za[0], zr, a_base);
+  u32x4 za[ZR][2];
+#pragma unroll
+  for (int d = 0; d < ZD; ++d) load_a(za[d], zr, a_base + (uint32_t)d * a_step);
 
   int it = 0;
   for (; it + RING <= iters; it += RING) {
 #pragma unroll
     for (int d = 0; d < RING; ++d) {
-      // A for the next step goes out before the stream load: loads complete in
-      // issue order, so waiting for it next step leaves the stream loads in flight.
-      load_a(za[(d + 1) & 1], zr, a_base + (uint32_t)(it + d + 1) * a_step);
+      // A goes out before the stream load: loads complete in issue order, so
+      // waiting for an A operand never waits for a younger stream load.
+      load_a(za[(d + ZD) % ZR], zr, a_base + (uint32_t)(it + d + ZD) * a_step);
       load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off, nb);
-      mfma_step<BITS>(ring[d], za[d & 1], acc);
+      mfma_step<BITS>(ring[d], za[d % ZR], acc);
     }
   }
 #pragma unroll
   for (int d = 0; d < RING; ++d) {
     if (it + d < iters) {
-      load_a(za[(d + 1) & 1], zr, a_base + (uint32_t)(it + d + 1) * a_step);
-      mfma_step<BITS>(ring[d], za[d & 1], acc);
+      load_a(za[(d + ZD) % ZR], zr, a_base + (uint32_t)(it + d + ZD) * a_step);
+      mfma_step<BITS>(ring[d], za[d % ZR], acc);
     }
   }
 
