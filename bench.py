@@ -33,7 +33,8 @@ WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
 CPU_SAMPLE_STRIPS = 128
 WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
-KERNEL_SOURCES = ["exl3_device.hpp", "exl3_linear.hip"]
+KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip"]
+KERNEL_NAMES = {"dot2": "linear_kernel<{bits}, 8, {rows}>", "mfma": "linear_mfma_kernel<{bits}, 8>"}
 
 
 def kernel_source_hash() -> str:
@@ -52,15 +53,14 @@ def algorithmic_bytes(rows: int) -> dict:
     return {"stream": stream, "total": stream + z + y + svh}
 
 
-def load_traffic(rows: int):
+def load_traffic(engine: str, rows: int):
     """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
     if not TRAFFIC_FILE.exists():
         return None
     rec = json.loads(TRAFFIC_FILE.read_text())
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    per_rows = rec.get("per_launch_bytes", {}).get(str(rows))
-    return per_rows
+    return rec.get("per_launch_bytes", {}).get(f"{engine}:{rows}")
 
 
 def make_inputs(torch, dev, rows: int, copies: int):
@@ -197,27 +197,31 @@ def _counter_means(directory: Path, kernel_substr: str) -> dict:
 
 
 def ingest_counters(base: Path) -> dict:
-    """Build the traffic record from rocprofv3 --pmc runs under `base`:
-    copy_fetch/, copy_write/ (bench.py --calibrate-copy), r{R}_fetch/, r{R}_write/ (bench.py --rows R)."""
+    """Build the traffic record from rocprofv3 --pmc runs under `base`: copy_fetch/, copy_write/
+    (bench.py --calibrate-copy) and {engine}_r{R}_fetch/, {engine}_r{R}_write/ (bench.py --engine E --rows R)."""
     copy_fetch = _counter_means(base / "copy_fetch", "copy_kernel")["FETCH_SIZE"]
     copy_write = _counter_means(base / "copy_write", "copy_kernel")["WRITE_SIZE"]
     f_read = COPY_BYTES / (copy_fetch * 1024)
     f_write = COPY_BYTES / (copy_write * 1024)
     per = {}
-    for rows in (1, 16):
-        d_f, d_w = base / f"r{rows}_fetch", base / f"r{rows}_write"
-        if not d_f.exists():
-            continue
-        name = f"linear_kernel<{BITS}, 8, {rows}>"
-        fetch = _counter_means(d_f, name)["FETCH_SIZE"]
-        write = _counter_means(d_w, name)["WRITE_SIZE"]
-        per[str(rows)] = int(round(fetch * 1024 * f_read + write * 1024 * f_write))
+    raw = {}
+    for engine, pattern in KERNEL_NAMES.items():
+        for rows in (1, 16):
+            d_f, d_w = base / f"{engine}_r{rows}_fetch", base / f"{engine}_r{rows}_write"
+            if not d_f.exists():
+                continue
+            name = pattern.format(bits=BITS, rows=rows)
+            fetch = _counter_means(d_f, name)["FETCH_SIZE"]
+            write = _counter_means(d_w, name)["WRITE_SIZE"]
+            raw[f"{engine}:{rows}"] = {"FETCH_SIZE": fetch, "WRITE_SIZE": write}
+            per[f"{engine}:{rows}"] = int(round(fetch * 1024 * f_read + write * 1024 * f_write))
     rec = {
         "kernel_source_hash": kernel_source_hash(),
         "copy_kib_per_launch": {"FETCH_SIZE": copy_fetch, "WRITE_SIZE": copy_write},
         "scale": {"read": f_read, "write": f_write},
+        "linear_kib_per_launch": raw,
         "per_launch_bytes": per,
-        "algorithmic_bytes": {r: algorithmic_bytes(int(r))["total"] for r in per},
+        "algorithmic_bytes": {k: algorithmic_bytes(int(k.split(":")[1]))["total"] for k in per},
     }
     TRAFFIC_FILE.parent.mkdir(exist_ok=True)
     TRAFFIC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
@@ -272,7 +276,7 @@ def main() -> int:
     ab = algorithmic_bytes(rows)
     stream_gbps = ab["stream"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["total"] / (lin_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(rows)
+    traffic = load_traffic(engine, rows)
 
     extra = {}
     if not args.no_r16:
