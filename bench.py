@@ -33,8 +33,10 @@ WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
 CPU_SAMPLE_STRIPS = 128
 WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
-KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip"]
-KERNEL_NAMES = {"dot2": "linear_kernel<{bits}, 8, {rows}>", "mfma": "linear_mfma_kernel<{bits}, 8>"}
+KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip",
+                  "exl3_project.hip"]
+KERNEL_NAMES = {"dot2": "linear_kernel<{bits}, 8, {rows}>", "mfma": "linear_mfma_kernel<{bits}, 8>",
+                "fused": "project_kernel<{bits}, 8, {rows}>"}
 
 
 def kernel_source_hash() -> str:
@@ -86,12 +88,18 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, en
     z = torch.empty((rows, IN_DIM), dtype=torch.float16, device=xt.device)
     y = torch.empty((rows, OUT_DIM), dtype=torch.float32, device=xt.device)
     copies = len(trellis)
+    def step(i):
+        if engine == "fused":
+            tq.project(xt, suh_t, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+        else:
+            tq.rot_in(xt, suh_t, z)
+            tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+
     # At least `warmup` steps and at least WARMUP_S seconds, so clocks settle first.
     t_start = time.perf_counter()
     i = 0
     while i < warmup or time.perf_counter() - t_start < WARMUP_S:
-        tq.rot_in(xt, suh_t, z)
-        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+        step(i)
         i += 1
         if i % 64 == 0:
             torch.cuda.synchronize()
@@ -103,9 +111,13 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, en
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
-        tq.rot_in(xt, suh_t, z)
-        ev[i][0].record(stream)
-        tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+        if engine == "fused":
+            ev[i][0].record(stream)
+            tq.project(xt, suh_t, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+        else:
+            tq.rot_in(xt, suh_t, z)
+            ev[i][0].record(stream)
+            tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
         ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -234,8 +246,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", type=int, default=1, help="rows of the headline region")
-    ap.add_argument("--engine", choices=["dot2", "mfma"], default="dot2",
-                    help="linear engine of the headline: v_dot2 chains or matrix cores")
+    ap.add_argument("--engine", choices=["dot2", "mfma", "fused"], default="dot2",
+                    help="headline path: rot_in + v_dot2 linear, rot_in + matrix-core linear, or the "
+                         "single-launch projection (rot_in fused into the v_dot2 linear)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
@@ -282,8 +295,8 @@ def main() -> int:
     if not args.no_r16:
         # Both engines at 1 and 16 rows, same inputs and protocol (the headline is one of them).
         table = {}
-        for eng in ("dot2", "mfma"):
-            for r in (1, 16):
+        for eng in ("dot2", "mfma", "fused"):
+            for r in ((1, 2) if eng == "fused" else (1, 16)):
                 t, l, _, _ = time_steps(torch, tq, trellis, xt[:r].contiguous(), suh_t, svh_t, args.steps,
                                         args.warmup, eng)
                 abr = algorithmic_bytes(r)
@@ -330,8 +343,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": (f"tf_exl3::linear_kernel<{BITS}, 8, {rows}>" if engine == "dot2"
-                       else f"tf_exl3::linear_mfma_kernel<{BITS}, 8>"),
+            "kernel": "tf_exl3::" + KERNEL_NAMES[engine].format(bits=BITS, rows=rows),
             "kernel_ms": round(lin_avg_ms, 5),
             "kernel_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
             "bytes_per_launch": ab["total"],

@@ -126,6 +126,26 @@ int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint1
                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                         int waves, void* stream);
 
+/*
+ * project: rot_in and the linear in one launch, y = linear(rot_in(x)).
+ * Every workgroup rotates its pass's rows into LDS with the same arithmetic as
+ * tf_exl3_rot_in and then runs tf_exl3_linear's own tile-row walk, so y is bit
+ * for bit what tf_exl3_rot_in followed by tf_exl3_linear gives, with one launch
+ * and no z buffer. Each workgroup recomputes the rotation of its rows, which
+ * pays at one or two decode rows; passes hold as many rows as fit in 48 KiB of
+ * LDS (tf_exl3_project_pass_rows), each pass streaming the weights once.
+ *
+ *  x       [rows][in_dim], element type x_dtype; suh [in_dim] fp16
+ *  trellis, svh, y, y_dtype, waves: as tf_exl3_linear; y must not overlap any input
+ */
+int tf_exl3_project(int bits, int rows, int in_dim, int out_dim, const void* x, int x_dtype,
+                    const uint16_t* suh, const uint32_t* trellis, const uint16_t* svh, void* y,
+                    int y_dtype, int waves, void* stream);
+
+/* Rows per pass tf_exl3_project uses for these arguments (host only), or a refusal:
+ * TF_E_SHAPE if even one row does not fit, TF_E_ROWS, TF_E_WAVES. */
+int tf_exl3_project_pass_rows(int rows, int in_dim, int out_dim, int waves);
+
 /* Launch plan the linear would use (host only; no GPU needed). */
 typedef struct {
   int width_index;    /* position of bits in {2, 3, 4, 5, 6, 8} */

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     header_functions,
     linear,
     linear_plan,
+    project,
+    project_pass_rows,
     load,
     rot_in,
     status_string,

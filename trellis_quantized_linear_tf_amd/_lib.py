@@ -52,6 +52,8 @@ SIGNATURES = {
     "tf_exl3_rot_in": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "tf_exl3_linear": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_linear_mfma": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_project": (_I, [_I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_project_pass_rows": (_I, [_I, _I, _I, _I]),
     "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "tf_exl3_trellis_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "tf_exl3_status_string": (ctypes.c_char_p, [_I]),
@@ -172,6 +174,23 @@ def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, wav
     _check(fn(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y), _dt_code(y.dtype), waves,
               _stream(z)))
     return y
+
+
+def project(x, suh, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0):
+    """y = linear(rot_in(x)) in one launch (bit-identical to rot_in then linear with engine "dot2")."""
+    torch = _torch()
+    rows, in_dim = x.shape
+    if y is None:
+        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=x.device)
+    _check(load().tf_exl3_project(bits, rows, in_dim, out_dim, _ptr(x), _dt_code(x.dtype), _ptr(suh),
+                                  _ptr(trellis), _ptr(svh), _ptr(y), _dt_code(y.dtype), waves, _stream(x)))
+    return y
+
+
+def project_pass_rows(rows: int, in_dim: int, out_dim: int, waves: int = 0) -> int:
+    r = load().tf_exl3_project_pass_rows(rows, in_dim, out_dim, waves)
+    _check(min(r, 0))
+    return r
 
 
 def debug_decode_states(states):

@@ -158,6 +158,38 @@ int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint1
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 
+int tf_exl3_project_pass_rows(int rows, int in_dim, int out_dim, int waves) {
+  if (!dim_ok(in_dim) || !dim_ok(out_dim)) return TF_E_SHAPE;
+  if (rows < 0) return TF_E_ROWS;
+  const int w = plan_waves(out_dim, waves);
+  if (w < 0) return TF_E_WAVES;
+  const int p = tf_exl3::project_pass_rows(rows, w, in_dim);
+  return p > 0 ? p : TF_E_SHAPE;
+}
+
+int tf_exl3_project(int bits, int rows, int in_dim, int out_dim, const void* x, int x_dtype, const uint16_t* suh,
+                    const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
+  tf_exl3_plan plan;
+  const int st = tf_exl3_linear_plan(bits, rows, in_dim, out_dim, waves, &plan);
+  if (st != TF_OK) return st;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return TF_E_DTYPE;
+  const int pass_rows = tf_exl3::project_pass_rows(rows, plan.waves, in_dim);
+  if (pass_rows == 0) return TF_E_SHAPE;
+  if (rows == 0) return TF_OK;
+  if (x == nullptr || suh == nullptr || trellis == nullptr || svh == nullptr || y == nullptr) return TF_E_NULL;
+  if (!aligned(x, elem_size(x_dtype)) || !aligned(suh, 2) || !aligned(trellis, 16) || !aligned(svh, 2) ||
+      !aligned(y, elem_size(y_dtype)))
+    return TF_E_ALIGN;
+  const size_t ny = (size_t)rows * (size_t)out_dim * elem_size(y_dtype);
+  if (overlap(y, ny, x, (size_t)rows * in_dim * elem_size(x_dtype)) || overlap(y, ny, suh, (size_t)in_dim * 2) ||
+      overlap(y, ny, trellis, (size_t)stream_bytes(bits, in_dim, out_dim)) ||
+      overlap(y, ny, svh, (size_t)out_dim * 2))
+    return TF_E_ALIAS;
+  const hipError_t e = tf_exl3::launch_project(bits, plan.waves, pass_rows, rows, in_dim, out_dim, x, x_dtype, suh,
+                                               trellis, svh, y, y_dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
 int tf_exl3_debug_decode_states(const uint16_t* states, uint16_t* w, int n, void* stream) {
   if (n < 0) return TF_E_SHAPE;
   if (n == 0) return TF_OK;

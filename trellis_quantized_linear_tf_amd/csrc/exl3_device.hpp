@@ -161,4 +161,53 @@ __device__ __forceinline__ void fwht128_wave(float& v0, float& v1) {
   v1 = a - b;
 }
 
+// ---------------------------------------------------------------------------
+// rot_in on one 128-block held by one wave: lane l gets elements l and l + 64.
+//   p = RN32(x * suh); butterflies (fwht128_wave); RN32(p * s); RN16 once.
+// The fp32 values pass an empty register barrier after the product and after
+// the scale, so neither is fused into its consumer (no single-rounding
+// multiply-and-convert). Both the rot_in kernel and the fused projection call
+// this, so they produce the same bits.
+template <int XDT>
+__device__ __forceinline__ float load_in(const void* __restrict__ x, size_t i) {
+  if constexpr (XDT == 0) {  // TF_DT_F32
+    return static_cast<const float*>(x)[i];
+  } else if constexpr (XDT == 1) {  // TF_DT_F16
+    return f16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+  } else {  // TF_DT_BF16
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+  }
+}
+
+// The arithmetic after the loads: p = RN32(x * suh), butterflies, RN32(p * s), RN16.
+__device__ __forceinline__ void rot_in_math(float x0, float x1, float g0, float g1, uint16_t& z0, uint16_t& z1) {
+  float v0 = opaque(x0 * g0);
+  float v1 = opaque(x1 * g1);
+  fwht128_wave(v0, v1);
+  const float s = bits_to_f32(kScaleBits);
+  v0 = opaque(v0 * s);
+  v1 = opaque(v1 * s);
+  z0 = f32_to_f16_bits(v0);
+  z1 = f32_to_f16_bits(v1);
+}
+
+// x + base is the block's first element, suh + col0 its first sign.
+template <int XDT>
+__device__ __forceinline__ void rot_in_block(const void* __restrict__ x, size_t base,
+                                             const uint16_t* __restrict__ suh, int col0, int lane,
+                                             uint16_t& z0, uint16_t& z1) {
+  rot_in_math(load_in<XDT>(x, base + lane), load_in<XDT>(x, base + lane + 64),
+              f16_bits_to_f32(suh[col0 + lane]), f16_bits_to_f32(suh[col0 + lane + 64]), z0, z1);
+}
+
+// Raw element of x (fp32 bits, or fp16/bf16 bits) and its widening, split so a
+// wave can issue the loads of several blocks before using any of them.
+__device__ __forceinline__ uint32_t load_raw(const void* __restrict__ x, int x_dtype, size_t i) {
+  return x_dtype == 0 ? static_cast<const uint32_t*>(x)[i] : (uint32_t) static_cast<const uint16_t*>(x)[i];
+}
+
+__device__ __forceinline__ float widen_raw(uint32_t v, int x_dtype) {
+  return x_dtype == 0 ? bits_to_f32(v) : x_dtype == 1 ? f16_bits_to_f32((uint16_t)v) : bf16_bits_to_f32((uint16_t)v);
+}
+
 }  // namespace tf_exl3

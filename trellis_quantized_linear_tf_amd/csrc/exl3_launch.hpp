@@ -15,6 +15,33 @@ inline int rows_bucket(int rows) {
 // LDS bytes of one linear block: the waves' partial sums [waves][rows][128] fp32.
 inline int linear_lds_bytes(int waves, int rows_cap) { return waves * rows_cap * 128 * 4; }
 
+// Fused projection: LDS of one workgroup holds its pass's z rows (fp16) and the
+// waves' partial sums; passes carry as many rows (1, 2, 4, 8 or 16) as fit in
+// kProjectLdsBudget, so several workgroups still share a CU.
+constexpr size_t kProjectLdsBudget = 48 * 1024;
+
+inline size_t project_lds_bytes(int waves, int rows_cap, int in_dim) {
+  return (size_t)rows_cap * in_dim * 2 + (size_t)waves * rows_cap * 128 * 4;
+}
+
+// Rows per pass of the fused projection for `rows` rows (0 if even one row does not fit).
+inline int project_pass_rows(int rows, int waves, int in_dim) {
+  int cap = 0;
+  for (int nr = 16; nr >= 1; nr /= 2) {
+    if (project_lds_bytes(waves, nr, in_dim) <= kProjectLdsBudget) {
+      cap = nr;
+      break;
+    }
+  }
+  if (cap == 0 || rows <= 0) return cap;
+  const int want = rows_bucket(rows < cap ? rows : cap);
+  return want < cap ? want : cap;
+}
+
+hipError_t launch_project(int bits, int waves, int nr_cap, int rows, int in_dim, int out_dim, const void* x,
+                          int x_dtype, const uint16_t* suh, const uint32_t* trellis, const uint16_t* svh, void* y,
+                          int y_dtype, hipStream_t stream);
+
 hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,
                          int in_dim, hipStream_t stream);
 

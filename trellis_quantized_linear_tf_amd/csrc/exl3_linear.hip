@@ -25,32 +25,12 @@
 
 namespace tf_exl3 {
 
-// One tile row of the strip for one wave: decode 32 weights per lane and chain
-// the dot products of every row.
-template <int BITS, int WAVES, int NR>
-__device__ __forceinline__ void tile_row_step(const uint32_t (&w)[BITS + 1], int i,
-                                              const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
-  half2_t wp[2][8];
-  decode_lane<BITS>(w, wp);
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint32_t* zp = zrow[r] + i * (WAVES * 8);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const half2_t zz = __builtin_bit_cast(half2_t, zp[p]);
-      acc[r][0] = __builtin_amdgcn_fdot2(zz, wp[0][p], acc[r][0], false);
-      acc[r][1] = __builtin_amdgcn_fdot2(zz, wp[1][p], acc[r][1], false);
-    }
-  }
-}
-
 template <int BITS, int WAVES, int NR>
 __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __restrict__ z,
                                                               const uint32_t* __restrict__ trellis,
                                                               const uint16_t* __restrict__ svh,
                                                               void* __restrict__ y, int y_dtype,
                                                               int rows, int in_dim, int out_dim) {
-  constexpr int PF = prefetch_depth<BITS>();
   __shared__ float partial[WAVES * NR * kBlock];
 
   const int lane = __lane_id();
@@ -82,29 +62,9 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r][0] = acc[r][1] = 0.0f;
 
-  // Step i (0 <= i < iters) is tile row kt = wave + i * WAVES. A ring of PF + 1
-  // slots keeps PF steps in flight: step i decodes slot i % (PF + 1) while the
-  // load for step i + PF goes to the slot step i - 1 has just freed. Addresses
-  // past the last step are clamped to it, so the ring needs no branches and the
-  // wait counts stay exact.
-  constexpr int RING = PF + 1;
-  auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
-  uint32_t ring[RING][BITS + 1];
-#pragma unroll
-  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
-
-  int it = 0;
-  for (; it + RING <= iters; it += RING) {
-#pragma unroll
-    for (int d = 0; d < RING; ++d) {
-      load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off, nb);
-      tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < RING; ++d) {
-    if (it + d < iters) tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
-  }
+  StreamWalk<BITS, WAVES, NR> walk{tp, step_words, off, nb, iters};
+  walk.prime();
+  walk.run(zrow, acc);
 
   // Cross-wave sums in wave order, then the output rotation, scale and svh.
 #pragma unroll

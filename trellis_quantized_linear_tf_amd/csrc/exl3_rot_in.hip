@@ -18,17 +18,6 @@ namespace tf_exl3 {
 constexpr int kRotWaves = 4;
 
 template <int XDT>
-__device__ __forceinline__ float load_in(const void* __restrict__ x, size_t i) {
-  if constexpr (XDT == TF_DT_F32) {
-    return static_cast<const float*>(x)[i];
-  } else if constexpr (XDT == TF_DT_F16) {
-    return f16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
-  } else {
-    return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
-  }
-}
-
-template <int XDT>
 __global__ __launch_bounds__(kWave* kRotWaves) void rot_in_kernel(const void* __restrict__ x,
                                                                   const uint16_t* __restrict__ suh,
                                                                   uint16_t* __restrict__ z,
@@ -39,18 +28,10 @@ __global__ __launch_bounds__(kWave* kRotWaves) void rot_in_kernel(const void* __
   if (blk >= n_blocks) return;
   const int kb = (int)(blk % blocks_per_row);
   const size_t base = (size_t)blk * kBlock;  // row * in_dim + kb * 128
-  const int col = kb * kBlock + lane;
-
-  const float p0 = load_in<XDT>(x, base + lane) * f16_bits_to_f32(suh[col]);
-  const float p1 = load_in<XDT>(x, base + lane + 64) * f16_bits_to_f32(suh[col + 64]);
-  float v0 = opaque(p0);
-  float v1 = opaque(p1);
-  fwht128_wave(v0, v1);
-  const float s = bits_to_f32(kScaleBits);
-  v0 = opaque(v0 * s);
-  v1 = opaque(v1 * s);
-  z[base + lane] = f32_to_f16_bits(v0);
-  z[base + lane + 64] = f32_to_f16_bits(v1);
+  uint16_t z0, z1;
+  rot_in_block<XDT>(x, base, suh, kb * kBlock, lane, z0, z1);
+  z[base + lane] = z0;
+  z[base + lane + 64] = z1;
 }
 
 hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,

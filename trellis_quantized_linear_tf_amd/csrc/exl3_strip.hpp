@@ -31,6 +31,67 @@ __device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint
   dst[BITS] = __builtin_nontemporal_load(p + nb);
 }
 
+// One tile row of the strip for one wave: decode 32 weights per lane and chain
+// the dot products of every row.
+template <int BITS, int WAVES, int NR>
+__device__ __forceinline__ void tile_row_step(const uint32_t (&w)[BITS + 1], int i,
+                                              const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
+  half2_t wp[2][8];
+  decode_lane<BITS>(w, wp);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t* zp = zrow[r] + i * (WAVES * 8);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const half2_t zz = __builtin_bit_cast(half2_t, zp[p]);
+      acc[r][0] = __builtin_amdgcn_fdot2(zz, wp[0][p], acc[r][0], false);
+      acc[r][1] = __builtin_amdgcn_fdot2(zz, wp[1][p], acc[r][1], false);
+    }
+  }
+}
+
+// The wave's walk over its tile rows for the v_dot2 engine. Step i (0 <= i <
+// iters) is tile row kt = wave + i * WAVES. A ring of PF + 1 slots keeps PF steps
+// in flight: step i decodes slot i % (PF + 1) while the load for step i + PF goes
+// to the slot step i - 1 has just freed. Addresses past the last step are
+// clamped to it, so the ring needs no branches and the wait counts stay exact.
+// prime() issues the first PF loads; run() walks all steps. zrow[r] points at
+// row r's inputs as (k, k+1) dword pairs, offset to this wave's first tile row
+// (global memory or LDS).
+template <int BITS, int WAVES, int NR>
+struct StreamWalk {
+  static constexpr int PF = prefetch_depth<BITS>();
+  static constexpr int RING = PF + 1;
+  const uint32_t* __restrict__ tp;
+  size_t step_words;
+  int off, nb, iters;
+  uint32_t ring[RING][BITS + 1];
+
+  __device__ __forceinline__ const uint32_t* share(int i) const {
+    return tp + (size_t)min(i, iters - 1) * step_words;
+  }
+
+  __device__ __forceinline__ void prime() {
+#pragma unroll
+    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
+  }
+
+  __device__ __forceinline__ void run(const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
+    int it = 0;
+    for (; it + RING <= iters; it += RING) {
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off, nb);
+        tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < RING; ++d) {
+      if (it + d < iters) tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
+    }
+  }
+};
+
 __device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, size_t i, float v) {
   if (y_dtype == TF_DT_F32) {
     static_cast<float*>(y)[i] = v;
