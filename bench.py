@@ -36,7 +36,8 @@ TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
 KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip",
                   "exl3_project.hip"]
 KERNEL_NAMES = {"dot2": "linear_kernel<{bits}, 8, {rows}>", "mfma": "linear_mfma_kernel<{bits}, 8>",
-                "fused": "project_kernel<{bits}, 8, {rows}>"}
+                "fused": "project_kernel<{bits}, 8, {rows}>", "prompt": "linear_kernel<{bits}, 8, 32>"}
+PROMPT_ROWS = 128
 
 
 def kernel_source_hash() -> str:
@@ -246,9 +247,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", type=int, default=1, help="rows of the headline region")
-    ap.add_argument("--engine", choices=["dot2", "mfma", "fused"], default="dot2",
-                    help="headline path: rot_in + v_dot2 linear, rot_in + matrix-core linear, or the "
-                         "single-launch projection (rot_in fused into the v_dot2 linear)")
+    ap.add_argument("--engine", choices=["dot2", "mfma", "fused", "prompt"], default="dot2",
+                    help="headline path: rot_in + v_dot2 linear, rot_in + matrix-core linear, the "
+                         "single-launch projection (rot_in fused into the v_dot2 linear), or rot_in + the "
+                         "prompt path (32-row passes, bit-equal to the v_dot2 linear)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
@@ -309,6 +311,22 @@ def main() -> int:
                     "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
                     "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 }
+        # The prompt path against the decode linear on a 128-row prompt (fewer steps: ~2 ms each).
+        import numpy as np
+
+        import synth
+
+        xp = synth.rows(synth.seed_for(WORKLOAD_ID, synth.STREAM_ROWS), PROMPT_ROWS, IN_DIM, "f16", 0.5)
+        xpt = torch.from_numpy(xp.view(np.int16)).to(dev).view(torch.float16)
+        psteps = max(10, args.steps // 10)
+        for eng in ("dot2", "prompt"):
+            t, l, _, _ = time_steps(torch, tq, trellis, xpt, suh_t, svh_t, psteps, args.warmup, eng)
+            table[f"{eng}_rows{PROMPT_ROWS}"] = {
+                "ms_per_step": round(t / psteps, 5),
+                "rows_per_s": round(PROMPT_ROWS / (t / psteps * 1e-3), 1),
+                "linear_ms": round(sum(l) / len(l), 5),
+                "steps": psteps,
+            }
         extra["engines"] = table
 
     ceiling = read_ceiling(torch, tq, dev)

@@ -113,6 +113,20 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
                    int waves, void* stream);
 
 /*
+ * linear_prompt: the prompt path, bit-equal to tf_exl3_linear (TensorFold pull
+ * request "hip exl3: the input rotation and trellis linear for decode rows",
+ * "Known limits": the prompt path that follows the decode rows is to give the
+ * same bits as this linear). Same arguments, refusals, stream format, waves and
+ * summation order as tf_exl3_linear; full passes carry 32 rows instead of 16,
+ * so each tile row is decoded once for twice the rows, and the remaining
+ * rows % 32 run as tf_exl3_linear's passes. Every output row is bit-identical
+ * to tf_exl3_linear's for the same (z row, trellis, svh, waves).
+ */
+int tf_exl3_linear_prompt(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                          int waves, void* stream);
+
+/*
  * linear_mfma: the same projection with the same arguments, refusals, stream
  * format and finish, but the sums over k run on the matrix cores
  * (v_mfma_f32_32x32x16_f16) instead of v_dot2 chains, so the vector ALUs only

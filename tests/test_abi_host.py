@@ -83,8 +83,9 @@ def test_plan_refusals(lib, args, code):
 FAKE = 0x7F0000000000  # never dereferenced: every call below is refused on the host
 
 
-def test_linear_refusals(lib):
-    f = lib.tf_exl3_linear
+@pytest.mark.parametrize("entry", ["tf_exl3_linear", "tf_exl3_linear_mfma", "tf_exl3_linear_prompt"])
+def test_linear_refusals(lib, entry):
+    f = getattr(lib, entry)
     ok = dict(bits=4, rows=2, k=256, n=256, z=FAKE, t=FAKE + 0x100000, s=FAKE + 0x200000, y=FAKE + 0x300000,
               dt=0, w=0)
 

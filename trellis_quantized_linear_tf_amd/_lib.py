@@ -52,6 +52,7 @@ SIGNATURES = {
     "tf_exl3_rot_in": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "tf_exl3_linear": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_linear_mfma": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_linear_prompt": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_project": (_I, [_I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_project_pass_rows": (_I, [_I, _I, _I, _I]),
     "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
@@ -157,20 +158,22 @@ def rot_in(x, suh, z=None):
     return z
 
 
-ENGINES = ("dot2", "mfma")
+ENGINES = ("dot2", "mfma", "prompt")
 
 
 def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0,
            engine: str = "dot2"):
     """y[rows][out_dim] = the trellis linear of fp16 z [rows][in_dim] (trellis: uint8/int32 stream).
-    engine "dot2" runs tf_exl3_linear, "mfma" runs tf_exl3_linear_mfma."""
+    engine "dot2" runs tf_exl3_linear, "mfma" tf_exl3_linear_mfma and "prompt"
+    tf_exl3_linear_prompt (32-row passes, bit-equal to "dot2")."""
     torch = _torch()
     rows, in_dim = z.shape
     if y is None:
         y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
     if engine not in ENGINES:
         raise ValueError(f"engine must be one of {ENGINES}")
-    fn = load().tf_exl3_linear if engine == "dot2" else load().tf_exl3_linear_mfma
+    lib = load()
+    fn = {"dot2": lib.tf_exl3_linear, "mfma": lib.tf_exl3_linear_mfma, "prompt": lib.tf_exl3_linear_prompt}[engine]
     _check(fn(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y), _dt_code(y.dtype), waves,
               _stream(z)))
     return y

@@ -148,6 +148,17 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 
+int tf_exl3_linear_prompt(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int waves,
+                          void* stream) {
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK || rows == 0) return st;
+  const hipError_t e = tf_exl3::launch_linear_prompt(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh,
+                                                     y, y_dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
 int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
                         const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
   tf_exl3_plan plan;

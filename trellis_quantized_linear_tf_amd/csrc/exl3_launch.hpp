@@ -49,6 +49,13 @@ hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim,
                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                          hipStream_t stream);
 
+// Rows per full pass of the prompt path (the rest runs as decode passes).
+constexpr int kPromptRowsPerPass = 32;
+
+hipError_t launch_linear_prompt(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                                const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                                hipStream_t stream);
+
 hipError_t launch_linear_mfma(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                               const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                               hipStream_t stream);

@@ -1,4 +1,5 @@
-// The trellis linear for 1..16 decode rows per pass.
+// The trellis linear for 1..16 decode rows per pass, and the prompt path's
+// 32-row passes of the same kernel.
 //
 // TensorFold pull request "hip exl3: the input rotation and trellis linear for
 // decode rows", "What this changes": a lane decodes its 16 x 16 tile values with
@@ -20,6 +21,16 @@
 //    one wave per row then runs the 128-point butterflies, the scale and svh.
 // A row's chain is: for each of its wave's tile rows in ascending kt, the pairs
 // p = 0..7 in ascending k; it is the same in every row-capacity variant.
+//
+// Prompt path (the same page, "Known limits": prompt rows must come out
+// bit-equal to this linear): full passes of 32 rows, so each tile row is decoded
+// once for twice the rows. A 32-row step needs 256 dwords of z, more than the
+// scalar registers hold, so prompt_kernel brings each wave's z slice for a step
+// (32 rows x 16 k) in with one 16-byte vector load per lane, one step ahead and
+// ahead of the stream loads, parks it in a wave-private LDS slot and reads each
+// row back as a broadcast. The dot2 chains, their order and the finish are the
+// decode linear's, hence the same bits. The finish runs in two rounds of 16
+// rows so the partial sums stay at 64 KiB of LDS.
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
@@ -31,12 +42,12 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ svh,
                                                               void* __restrict__ y, int y_dtype,
                                                               int rows, int in_dim, int out_dim) {
-  __shared__ float partial[WAVES * NR * kBlock];
+  __shared__ float partial[WAVES * (NR < kRowsPerPass ? NR : kRowsPerPass) * kBlock];
 
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int strip = blockIdx.x;
-  const int r0 = blockIdx.y * kRowsPerPass;
+  const int r0 = blockIdx.y * NR;
   const int nr = min(NR, rows - r0);
   const int iters = in_dim / 16 / WAVES;
 
@@ -67,16 +78,7 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   walk.run(zrow, acc);
 
   // Cross-wave sums in wave order, then the output rotation, scale and svh.
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float2 v;
-    v.x = acc[r][0];
-    v.y = acc[r][1];
-    *reinterpret_cast<float2*>(&partial[(wave * NR + r) * kBlock + 2 * lane]) = v;
-  }
-  __syncthreads();
-
-  finish_strip<WAVES>(partial, NR, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
+  finish_pass<WAVES, NR>(acc, partial, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
 template <int BITS, int WAVES>
@@ -141,6 +143,157 @@ hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim,
     case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
     case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
     default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  }
+}
+
+// The prompt kernel's walk: the stream ring of StreamWalk with PF = 2 (a 32-row
+// step is long enough that two tile rows in flight cover the stream's latency),
+// plus the wave's z slice for each step staged through a wave-private LDS slot.
+template <int BITS, int WAVES, int NR>
+struct PromptWalk {
+  static_assert(2 * NR <= kWave, "a lane stages one (row, k-half) of the step's z");
+  static constexpr int PF = 2;
+  static constexpr int RING = PF + 1;
+  const uint32_t* __restrict__ tp;
+  size_t step_words;
+  int off, nb, iters;
+  const uint4* __restrict__ zsrc;  // this lane's 16 bytes of z for step 0
+  uint4* zslot;                    // the wave's LDS slot: row r, k-half h at [2r + h]
+  bool stager;                     // lane < 2 * NR
+  uint32_t ring[RING][BITS + 1];
+  uint4 zn;
+
+  __device__ __forceinline__ const uint32_t* share(int i) const {
+    return tp + (size_t)min(i, iters - 1) * step_words;
+  }
+  __device__ __forceinline__ uint4 zload(int i) const { return zsrc[(size_t)min(i, iters - 1) * (WAVES * 2)]; }
+
+  __device__ __forceinline__ void prime() {
+    zn = zload(0);
+#pragma unroll
+    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
+  }
+
+  // Step i, decoding ring slot D = i % RING; the load for step i + PF refills
+  // the slot step i - 1 freed.
+  template <int D>
+  __device__ __forceinline__ void step(int i, float (&acc)[NR][2]) {
+    const uint4 zc = zn;
+    zn = zload(i + 1);  // issued before the next stream load: loads complete in order
+    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off, nb);
+    if (2 * NR == kWave || stager) zslot[__lane_id()] = zc;
+    half2_t wp[2][8];
+    decode_lane<BITS>(ring[D], wp);
+    // Row r + 1's z is read while row r's chains run. The empty asm after row
+    // r takes its accumulators and orders memory, so the chains cannot sink
+    // below later rows' reads and at most two rows of z (16 registers) are live.
+    uint4 lo = zslot[0];
+    uint4 hi = zslot[1];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t zp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (r + 1 < NR) {
+        lo = zslot[2 * r + 2];
+        hi = zslot[2 * r + 3];
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const half2_t zz = __builtin_bit_cast(half2_t, zp[p]);
+        acc[r][0] = __builtin_amdgcn_fdot2(zz, wp[0][p], acc[r][0], false);
+        acc[r][1] = __builtin_amdgcn_fdot2(zz, wp[1][p], acc[r][1], false);
+      }
+      asm volatile("" : "+v"(acc[r][0]), "+v"(acc[r][1])::"memory");
+    }
+  }
+
+  __device__ __forceinline__ void run(float (&acc)[NR][2]) {
+    static_assert(RING == 3, "the step lists below name the ring slots");
+    int it = 0;
+    for (; it + RING <= iters; it += RING) {
+      step<0>(it, acc);
+      step<1>(it + 1, acc);
+      step<2>(it + 2, acc);
+    }
+    if (it < iters) step<0>(it, acc);
+    if (it + 1 < iters) step<1>(it + 1, acc);
+  }
+};
+
+template <int BITS, int WAVES, int NR>
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void prompt_kernel(
+    const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
+    void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
+  __shared__ float partial[WAVES * kRowsPerPass * kBlock];
+  __shared__ uint4 zslot[WAVES][2 * NR];
+
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int strip = blockIdx.x;
+  const int r0 = blockIdx.y * NR;
+  const int nr = min(NR, rows - r0);
+  const int iters = in_dim / 16 / WAVES;
+  const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
+
+  // Lane l stages row min(l / 2, nr - 1), k-half l % 2 of tile row kt = wave + i * WAVES.
+  const int zr = min(lane >> 1, nr - 1);
+  PromptWalk<BITS, WAVES, NR> walk{
+      trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS,
+      (size_t)WAVES * row_words,
+      lane * BITS,
+      next_lane_in_tile(lane) * BITS,
+      iters,
+      reinterpret_cast<const uint4*>(z + (size_t)(r0 + zr) * in_dim + wave * 16 + (lane & 1) * 8),
+      zslot[wave],
+      lane < 2 * NR};
+
+  float acc[NR][2];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r][0] = acc[r][1] = 0.0f;
+  walk.prime();
+  walk.run(acc);
+
+  finish_pass<WAVES, NR>(acc, partial, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
+}
+
+template <int BITS, int WAVES>
+static hipError_t launch_prompt_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
+                                   const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                                   hipStream_t stream) {
+  const int full = rows / kPromptRowsPerPass;
+  const int rest = rows % kPromptRowsPerPass;
+  if (full > 0) {
+    hipLaunchKernelGGL((prompt_kernel<BITS, WAVES, kPromptRowsPerPass>), dim3(out_dim / kBlock, full),
+                       dim3(kWave * WAVES), 0, stream, z, trellis, svh, y, y_dtype, full * kPromptRowsPerPass,
+                       in_dim, out_dim);
+  }
+  if (rest > 0) {
+    const size_t off = (size_t)full * kPromptRowsPerPass;
+    void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
+                                      : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
+    return launch_bw<BITS, WAVES>(rest, in_dim, out_dim, z + off * in_dim, trellis, svh, yr, y_dtype, stream);
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_prompt_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                                  const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                                  hipStream_t stream) {
+  if (waves == 8) return launch_prompt_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  return launch_prompt_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+}
+
+hipError_t launch_linear_prompt(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                                const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                                hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  switch (bits) {
+    case 2: return launch_prompt_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 3: return launch_prompt_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 4: return launch_prompt_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 5: return launch_prompt_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 6: return launch_prompt_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    default: return launch_prompt_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
   }
 }
 

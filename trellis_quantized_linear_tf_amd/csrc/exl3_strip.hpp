@@ -133,4 +133,29 @@ __device__ __forceinline__ void finish_strip(const float* partial, int rstride, 
   }
 }
 
+// The end of a pass: the waves' sums (acc[r][c] = strip column 2*lane + c of
+// pass row r) through LDS and finish_strip, FR = min(NR, 16) rows per round so
+// `partial` ([WAVES][FR][128] fp32) stays at most 64 KiB.
+template <int WAVES, int NR>
+__device__ __forceinline__ void finish_pass(const float (&acc)[NR][2], float* partial, int wave, int lane,
+                                            int nr, int r0, int strip, int out_dim,
+                                            const uint16_t* __restrict__ svh, void* __restrict__ y,
+                                            int y_dtype) {
+  constexpr int FR = NR < kRowsPerPass ? NR : kRowsPerPass;
+#pragma unroll
+  for (int c = 0; c < NR; c += FR) {
+    if (c >= nr) break;  // block-uniform
+    if (c > 0) __syncthreads();  // the previous round has read partial
+#pragma unroll
+    for (int r = 0; r < FR; ++r) {
+      float2 v;
+      v.x = acc[c + r][0];
+      v.y = acc[c + r][1];
+      *reinterpret_cast<float2*>(&partial[(wave * FR + r) * kBlock + 2 * lane]) = v;
+    }
+    __syncthreads();
+    finish_strip<WAVES>(partial, FR, wave, lane, min(FR, nr - c), r0 + c, strip, out_dim, svh, y, y_dtype);
+  }
+}
+
 }  // namespace tf_exl3
