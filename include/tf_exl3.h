@@ -168,8 +168,10 @@ typedef struct {
   int grid_x;         /* blocks per pass = out_dim / 128 */
   int passes;         /* ceil(rows / 16) */
   int rows_last_pass; /* rows in the last pass (1..16), 0 when rows == 0 */
-  int rows_kernel;    /* row capacity of the kernel variant used for a full pass */
-  int lds_bytes;      /* LDS per block of a full pass */
+  int rows_kernel;    /* row capacity of the variant for the first pass: 1, 2, 4, 8, 12 or 16
+                         (up to 4 rows z arrives through scalar loads, above through LDS) */
+  int lds_bytes;      /* LDS per block of that pass: partial sums waves * min(rows_kernel, 16)
+                         * 512 bytes, plus z slots waves * 2 * rows_kernel * 16 bytes above 4 rows */
 } tf_exl3_plan;
 
 /* Fills *out with the plan for these arguments, or returns the refusal the linear

@@ -9,11 +9,22 @@ namespace tf_exl3 {
 
 // Row capacity of the linear kernel variant that serves `rows` (1..16) rows.
 inline int rows_bucket(int rows) {
-  return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
+  return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
 }
 
-// LDS bytes of one linear block: the waves' partial sums [waves][rows][128] fp32.
-inline int linear_lds_bytes(int waves, int rows_cap) { return waves * rows_cap * 128 * 4; }
+// Up to this many rows a pass takes z through scalar loads; above it, through
+// a wave-private LDS slot (one vector load per lane per tile row).
+constexpr int kScalarZRows = 4;
+
+// LDS bytes of one linear block: the waves' partial sums [waves][min(rows, 16)][128]
+// fp32, plus the z slots [waves][2 * rows] of 16 bytes when z goes through LDS.
+inline int linear_lds_bytes(int waves, int rows_cap) {
+  const int fr = rows_cap < 16 ? rows_cap : 16;
+  return waves * fr * 128 * 4 + (rows_cap > kScalarZRows ? waves * 2 * rows_cap * 16 : 0);
+}
+
+// Row capacity of the fused projection's variant for `rows` rows (powers of two).
+inline int pow2_bucket(int rows) { return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16; }
 
 // Fused projection: LDS of one workgroup holds its pass's z rows (fp16) and the
 // waves' partial sums; passes carry as many rows (1, 2, 4, 8 or 16) as fit in
@@ -34,7 +45,7 @@ inline int project_pass_rows(int rows, int waves, int in_dim) {
     }
   }
   if (cap == 0 || rows <= 0) return cap;
-  const int want = rows_bucket(rows < cap ? rows : cap);
+  const int want = pow2_bucket(rows < cap ? rows : cap);
   return want < cap ? want : cap;
 }
 

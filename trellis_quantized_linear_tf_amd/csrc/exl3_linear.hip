@@ -1,5 +1,5 @@
-// The trellis linear for 1..16 decode rows per pass, and the prompt path's
-// 32-row passes of the same kernel.
+// The trellis linear: 1..16 decode rows per pass, and the prompt path's 32-row
+// passes.
 //
 // TensorFold pull request "hip exl3: the input rotation and trellis linear for
 // decode rows", "What this changes": a lane decodes its 16 x 16 tile values with
@@ -8,29 +8,30 @@
 // sums, the output rotation and svh finish the block; no K split, no bias.
 //
 // Work layout on gfx950:
-//  - one workgroup per (128-column strip, pass of up to 16 rows);
+//  - one workgroup per (128-column strip, pass of rows);
 //  - the strip's tile row kt is 8 contiguous tiles = 256*BITS bytes, read by one
 //    wave as one coalesced load (BITS dwords per lane); lane l owns strip
 //    columns 2l and 2l+1;
 //  - wave w takes tile rows kt = w, w + WAVES, ... (in_dim/16 is a multiple of
-//    8, so every wave gets the same count), with a register ring of PF tile rows
-//    in flight;
-//  - z pairs are wave-uniform and come in through scalar loads, feeding
-//    v_dot2_f32_f16 as the SGPR operand;
+//    8, so every wave gets the same count), with a register ring of tile rows in
+//    flight;
+//  - z pairs are wave-uniform. For up to 4 rows a pass (linear_kernel) they come
+//    in through scalar loads and feed v_dot2_f32_f16 as the SGPR operand. For 8,
+//    12, 16 and 32 rows (linear_lds_kernel) a step's z (rows x 16 k) needs more
+//    scalar registers than a wave has, so each lane brings 16 bytes of it in
+//    with one vector load, one step ahead and ahead of the stream loads, the
+//    wave parks the slice in a private LDS slot and reads each row back as a
+//    broadcast;
 //  - the partial sums go through LDS and are added in wave order 0..WAVES-1;
-//    one wave per row then runs the 128-point butterflies, the scale and svh.
+//    one wave per row then runs the 128-point butterflies, the scale and svh
+//    (16 rows per round, so a 32-row pass keeps 64 KiB of partial sums).
 // A row's chain is: for each of its wave's tile rows in ascending kt, the pairs
-// p = 0..7 in ascending k; it is the same in every row-capacity variant.
+// p = 0..7 in ascending k; it is the same in every variant, whichever way z
+// arrives, so a row's bits never depend on the variant.
 //
 // Prompt path (the same page, "Known limits": prompt rows must come out
-// bit-equal to this linear): full passes of 32 rows, so each tile row is decoded
-// once for twice the rows. A 32-row step needs 256 dwords of z, more than the
-// scalar registers hold, so prompt_kernel brings each wave's z slice for a step
-// (32 rows x 16 k) in with one 16-byte vector load per lane, one step ahead and
-// ahead of the stream loads, parks it in a wave-private LDS slot and reads each
-// row back as a broadcast. The dot2 chains, their order and the finish are the
-// decode linear's, hence the same bits. The finish runs in two rounds of 16
-// rows so the partial sums stay at 64 KiB of LDS.
+// bit-equal to this linear): full passes of 32 rows decode each tile row once
+// for twice the rows; the remainder runs as decode passes.
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
@@ -81,76 +82,11 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   finish_pass<WAVES, NR>(acc, partial, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
-template <int BITS, int WAVES>
-static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
-                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
-                            hipStream_t stream) {
-  const int full = rows / kRowsPerPass;
-  const int rest = rows % kRowsPerPass;
-  const dim3 block(kWave * WAVES);
-  if (full > 0) {
-    hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 16>), dim3(out_dim / kBlock, full), block, 0,
-                       stream, z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim, out_dim);
-  }
-  if (rest > 0) {
-    const size_t off = (size_t)full * kRowsPerPass;
-    const uint16_t* zr = z + off * in_dim;
-    void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
-                                      : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
-    const dim3 grid(out_dim / kBlock, 1);
-    switch (rows_bucket(rest)) {
-      case 1:
-        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 1>), grid, block, 0, stream, zr, trellis, svh,
-                           yr, y_dtype, rest, in_dim, out_dim);
-        break;
-      case 2:
-        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 2>), grid, block, 0, stream, zr, trellis, svh,
-                           yr, y_dtype, rest, in_dim, out_dim);
-        break;
-      case 4:
-        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 4>), grid, block, 0, stream, zr, trellis, svh,
-                           yr, y_dtype, rest, in_dim, out_dim);
-        break;
-      case 8:
-        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 8>), grid, block, 0, stream, zr, trellis, svh,
-                           yr, y_dtype, rest, in_dim, out_dim);
-        break;
-      default:
-        hipLaunchKernelGGL((linear_kernel<BITS, WAVES, 16>), grid, block, 0, stream, zr, trellis,
-                           svh, yr, y_dtype, rest, in_dim, out_dim);
-        break;
-    }
-  }
-  return hipGetLastError();
-}
-
-template <int BITS>
-static hipError_t launch_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
-                           const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
-                           hipStream_t stream) {
-  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-}
-
-hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
-                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
-                         hipStream_t stream) {
-  if (rows == 0) return hipSuccess;
-  switch (bits) {
-    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-  }
-}
-
-// The prompt kernel's walk: the stream ring of StreamWalk with PF = 2 (a 32-row
+// The walk of linear_lds_kernel: the stream ring of StreamWalk with PF = 2 (a 32-row
 // step is long enough that two tile rows in flight cover the stream's latency),
 // plus the wave's z slice for each step staged through a wave-private LDS slot.
 template <int BITS, int WAVES, int NR>
-struct PromptWalk {
+struct LdsWalk {
   static_assert(2 * NR <= kWave, "a lane stages one (row, k-half) of the step's z");
   static constexpr int PF = 2;
   static constexpr int RING = PF + 1;
@@ -181,7 +117,7 @@ struct PromptWalk {
     const uint4 zc = zn;
     zn = zload(i + 1);  // issued before the next stream load: loads complete in order
     load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off, nb);
-    if (2 * NR == kWave || stager) zslot[__lane_id()] = zc;
+    if (stager) zslot[__lane_id()] = zc;
     half2_t wp[2][8];
     decode_lane<BITS>(ring[D], wp);
     // Row r + 1's z is read while row r's chains run. The empty asm after row
@@ -220,7 +156,7 @@ struct PromptWalk {
 };
 
 template <int BITS, int WAVES, int NR>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void prompt_kernel(
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_lds_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
   __shared__ float partial[WAVES * kRowsPerPass * kBlock];
@@ -236,7 +172,7 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
 
   // Lane l stages row min(l / 2, nr - 1), k-half l % 2 of tile row kt = wave + i * WAVES.
   const int zr = min(lane >> 1, nr - 1);
-  PromptWalk<BITS, WAVES, NR> walk{
+  LdsWalk<BITS, WAVES, NR> walk{
       trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS,
       (size_t)WAVES * row_words,
       lane * BITS,
@@ -255,6 +191,71 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   finish_pass<WAVES, NR>(acc, partial, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
+// One launch of the variant with row capacity NR: z through scalar loads for
+// NR <= kScalarZRows, else through LDS.
+template <int BITS, int WAVES, int NR>
+static void launch_nr(dim3 grid, const uint16_t* z, const uint32_t* trellis, const uint16_t* svh, void* y,
+                      int y_dtype, int rows, int in_dim, int out_dim, hipStream_t stream) {
+  if constexpr (NR <= kScalarZRows) {
+    hipLaunchKernelGGL((linear_kernel<BITS, WAVES, NR>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh,
+                       y, y_dtype, rows, in_dim, out_dim);
+  } else {
+    hipLaunchKernelGGL((linear_lds_kernel<BITS, WAVES, NR>), grid, dim3(kWave * WAVES), 0, stream, z, trellis,
+                       svh, y, y_dtype, rows, in_dim, out_dim);
+  }
+}
+
+template <int BITS, int WAVES>
+static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
+                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                            hipStream_t stream) {
+  const int full = rows / kRowsPerPass;
+  const int rest = rows % kRowsPerPass;
+  const int strips = out_dim / kBlock;
+  if (full > 0) {
+    launch_nr<BITS, WAVES, 16>(dim3(strips, full), z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim,
+                               out_dim, stream);
+  }
+  if (rest > 0) {
+    const size_t off = (size_t)full * kRowsPerPass;
+    const uint16_t* zr = z + off * in_dim;
+    void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
+                                      : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
+    const dim3 grid(strips, 1);
+    switch (rows_bucket(rest)) {
+      case 1: launch_nr<BITS, WAVES, 1>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      case 2: launch_nr<BITS, WAVES, 2>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      case 4: launch_nr<BITS, WAVES, 4>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      case 8: launch_nr<BITS, WAVES, 8>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      case 12: launch_nr<BITS, WAVES, 12>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      default: launch_nr<BITS, WAVES, 16>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                           const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                           hipStream_t stream) {
+  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+}
+
+hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                         hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  switch (bits) {
+    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  }
+}
+
 template <int BITS, int WAVES>
 static hipError_t launch_prompt_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
                                    const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
@@ -262,7 +263,7 @@ static hipError_t launch_prompt_bw(int rows, int in_dim, int out_dim, const uint
   const int full = rows / kPromptRowsPerPass;
   const int rest = rows % kPromptRowsPerPass;
   if (full > 0) {
-    hipLaunchKernelGGL((prompt_kernel<BITS, WAVES, kPromptRowsPerPass>), dim3(out_dim / kBlock, full),
+    hipLaunchKernelGGL((linear_lds_kernel<BITS, WAVES, kPromptRowsPerPass>), dim3(out_dim / kBlock, full),
                        dim3(kWave * WAVES), 0, stream, z, trellis, svh, y, y_dtype, full * kPromptRowsPerPass,
                        in_dim, out_dim);
   }
