@@ -35,8 +35,27 @@ WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
 KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip",
                   "exl3_project.hip"]
-KERNEL_NAMES = {"dot2": "linear_kernel<{bits}, 8, {rows}>", "mfma": "linear_mfma_kernel<{bits}, 8>",
-                "fused": "project_kernel<{bits}, 8, {rows}>", "prompt": "linear_kernel<{bits}, 8, 32>"}
+PROMPT_ROWS = 128
+# (engine, rows) regions whose HBM counters ingest_counters reads.
+COUNTER_REGIONS = [("dot2", 1), ("dot2", 16), ("mfma", 1), ("mfma", 16), ("fused", 1)]
+
+
+def _bucket(rows: int) -> int:
+    return next(c for c in (1, 2, 4, 8, 12, 16) if rows <= c)
+
+
+def kernel_name(engine: str, rows: int) -> str:
+    """The kernel that does the linear's work for `rows` rows on the LM head (first pass)."""
+    if engine == "mfma":
+        return f"linear_mfma_kernel<{BITS}, 8>"
+    if engine == "fused":
+        import trellis_quantized_linear_tf_amd as tq
+
+        return f"project_kernel<{BITS}, 8, {tq.project_pass_rows(rows, IN_DIM, OUT_DIM)}>"
+    if engine == "prompt" and rows >= 32:
+        return f"linear_lds_kernel<{BITS}, 8, 32>"
+    b = _bucket(min(rows, 16))
+    return f"linear_kernel<{BITS}, 8, {b}>" if b <= 4 else f"linear_lds_kernel<{BITS}, 8, {b}>"
 PROMPT_ROWS = 128
 
 
@@ -218,12 +237,10 @@ def ingest_counters(base: Path) -> dict:
     f_write = COPY_BYTES / (copy_write * 1024)
     per = {}
     raw = {}
-    for engine, pattern in KERNEL_NAMES.items():
-        for rows in (1, 16):
-            d_f, d_w = base / f"{engine}_r{rows}_fetch", base / f"{engine}_r{rows}_write"
-            if not d_f.exists():
-                continue
-            name = pattern.format(bits=BITS, rows=rows)
+    for engine, rows in COUNTER_REGIONS:
+        d_f, d_w = base / f"{engine}_r{rows}_fetch", base / f"{engine}_r{rows}_write"
+        if d_f.exists():
+            name = kernel_name(engine, rows)
             fetch = _counter_means(d_f, name)["FETCH_SIZE"]
             write = _counter_means(d_w, name)["WRITE_SIZE"]
             raw[f"{engine}:{rows}"] = {"FETCH_SIZE": fetch, "WRITE_SIZE": write}
@@ -361,7 +378,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "tf_exl3::" + KERNEL_NAMES[engine].format(bits=BITS, rows=rows),
+            "kernel": "tf_exl3::" + kernel_name(engine, rows),
             "kernel_ms": round(lin_avg_ms, 5),
             "kernel_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
             "bytes_per_launch": ab["total"],
