@@ -20,6 +20,10 @@ or value order, so this module fixes one concrete format (readings, in order):
      pairs are adjacent values.
   R4 tile order: tile (kt, nt) of an in_dim x out_dim matrix starts at word
      (kt * out_dim/16 + nt) * 8K (row-major tiles, the "tile layout").
+  R21 strips layout (the same section's identity test runs "at 8 waves on the
+     strips layout" without defining it): the same tiles, ordered so that each
+     128-column strip (8 tile columns) is one contiguous stream: tile (kt, nt)
+     starts at word ((nt div 8) * in_dim/16 + kt) * 8 + nt mod 8, times 8K.
   R5 codebook: x = (state * 0x9E3779) mod 2^32 (a 24-bit Fibonacci-hashing
      multiplier, floor(2^24 / golden ratio) rounded to odd); h = sum of the four
      bytes of x (0..1020); w = RN16((1024 + h) * A + B) with A = 0x1EEE and
@@ -163,3 +167,37 @@ def strip_tile_cols(strips) -> np.ndarray:
     """Tile columns of the given 128-column strips."""
     strips = np.asarray(strips, dtype=np.int64).reshape(-1)
     return (8 * strips[:, None] + np.arange(8)[None, :]).reshape(-1)
+
+
+# ---------------------------------------------------------------------------
+# The strips layout (R21).
+
+
+def strips_tile_offset(bits: int, in_dim: int, kt: int, nt: int) -> int:
+    """Word offset of tile (kt, nt) in the strips layout."""
+    strip, t = divmod(nt, 8)
+    return ((strip * (in_dim // 16) + kt) * 8 + t) * tile_words(bits)
+
+
+def _strips_tile_index(in_dim: int, out_dim: int) -> np.ndarray:
+    """[in_dim/16][out_dim/16] -> tile index (in tiles) in the strips layout."""
+    kt = np.arange(in_dim // 16, dtype=np.int64)[:, None]
+    nt = np.arange(out_dim // 16, dtype=np.int64)[None, :]
+    return ((nt // 8) * (in_dim // 16) + kt) * 8 + nt % 8
+
+
+def tiles_to_strips(trellis: np.ndarray, bits: int, in_dim: int, out_dim: int) -> np.ndarray:
+    """The stream in the strips layout: every tile copied to its strips-layout offset."""
+    grid = tile_grid(trellis, bits, in_dim, out_dim)
+    tw = tile_words(bits)
+    out = np.empty(grid.size, dtype=np.uint32)
+    out.reshape(-1, tw)[_strips_tile_index(in_dim, out_dim).reshape(-1)] = grid.reshape(-1, tw)
+    return out
+
+
+def strips_to_tiles(strips: np.ndarray, bits: int, in_dim: int, out_dim: int) -> np.ndarray:
+    """The stream in the tile layout (R4) from a strips-layout stream."""
+    tw = tile_words(bits)
+    src = np.asarray(strips, dtype=np.uint32).reshape(-1, tw)
+    assert src.size * 4 == trellis_bytes(bits, in_dim, out_dim)
+    return src[_strips_tile_index(in_dim, out_dim).reshape(-1)].reshape(-1)

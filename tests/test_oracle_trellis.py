@@ -152,3 +152,41 @@ def test_trellis_bytes():
     assert tr.trellis_bytes(4, 5120, 129280) == 330_956_800
     assert tr.trellis_bytes(8, 5120, 129280) == 661_913_600
     assert tr.trellis_bytes(3, 6144, 25600) == 58_982_400
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
+def test_strips_layout_places_each_tile(bits):
+    """Each tile, tagged with its (kt, nt), sits at the stated strips-layout offset, and
+    strip s's region holds exactly its 8 tile columns, tile rows in ascending kt."""
+    k, n = 64, 384
+    kt_n, nt_n, tw = k // 16, n // 16, 8 * bits
+    tiles = np.empty((kt_n, nt_n, tw), dtype=np.uint32)
+    for kt in range(kt_n):
+        for nt in range(nt_n):
+            tiles[kt, nt] = (kt << 16) | nt
+    strips = tr.tiles_to_strips(tiles.reshape(-1), bits, k, n)
+    for kt in range(kt_n):
+        for nt in range(nt_n):
+            o = tr.strips_tile_offset(bits, k, kt, nt)
+            assert np.all(strips[o : o + tw] == ((kt << 16) | nt))
+    region = kt_n * 8 * tw
+    for s in range(nt_n // 8):
+        tags = strips[s * region : (s + 1) * region : tw]
+        want = [(kt << 16) | (8 * s + t) for kt in range(kt_n) for t in range(8)]
+        assert tags.tolist() == want
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
+def test_strips_round_trip(bits):
+    k, n = 256, 640
+    stream = synth.trellis_words(3000 + bits, bits, k, n)
+    strips = tr.tiles_to_strips(stream, bits, k, n)
+    assert strips.size == stream.size and not np.array_equal(strips, stream)
+    assert np.array_equal(tr.strips_to_tiles(strips, bits, k, n), stream)
+    assert np.array_equal(np.sort(strips), np.sort(stream))
+
+
+def test_strips_layout_of_one_strip_is_the_tile_layout():
+    """With 128 columns there is one strip, and both layouts coincide."""
+    stream = synth.trellis_words(3100, 4, 512, 128)
+    assert np.array_equal(tr.tiles_to_strips(stream, 4, 512, 128), stream)
