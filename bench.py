@@ -264,10 +264,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", type=int, default=1, help="rows of the headline region")
-    ap.add_argument("--engine", choices=["dot2", "mfma", "fused", "prompt"], default="dot2",
+    ap.add_argument("--engine", choices=["dot2", "mfma", "fused", "prompt", "strips"], default="dot2",
                     help="headline path: rot_in + v_dot2 linear, rot_in + matrix-core linear, the "
                          "single-launch projection (rot_in fused into the v_dot2 linear), or rot_in + the "
-                         "prompt path (32-row passes, bit-equal to the v_dot2 linear)")
+                         "prompt path (32-row passes, bit-equal to the v_dot2 linear), or rot_in + the v_dot2 "
+                         "linear on the strips layout")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
@@ -301,8 +302,10 @@ def main() -> int:
     rows = args.rows
     trellis, xt, suh_t, svh_t, host = make_inputs(torch, dev, 16, copies=2)
     engine = args.engine
-    total_ms, lin_ms, wall, y = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t,
+    head = [tq.repack_strips(t, BITS, IN_DIM, OUT_DIM) for t in trellis] if engine == "strips" else trellis
+    total_ms, lin_ms, wall, y = time_steps(torch, tq, head, xt[:rows].contiguous(), suh_t, svh_t,
                                            args.steps, args.warmup, engine)
+    del head
     ms_per_step = total_ms / args.steps
     lin_avg_ms = sum(lin_ms) / len(lin_ms)
     ab = algorithmic_bytes(rows)
@@ -328,6 +331,24 @@ def main() -> int:
                     "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
                     "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 }
+        # The strips layout (each strip one contiguous stream), same stream repacked.
+        strips = [tq.repack_strips(t, BITS, IN_DIM, OUT_DIM) for t in trellis]
+        torch.cuda.synchronize()
+        for r in (1, 16):
+            t, l, _, _ = time_steps(torch, tq, strips, xt[:r].contiguous(), suh_t, svh_t, args.steps,
+                                    args.warmup, "strips")
+            abr = algorithmic_bytes(r)
+            l_avg = sum(l) / len(l)
+            table[f"strips_rows{r}"] = {
+                "ms_per_step": round(t / args.steps, 5),
+                "value": round(abr["stream"] / (t / args.steps * 1e-3) / 1e9, 2),
+                "rows_per_s": round(r / (t / args.steps * 1e-3), 1),
+                "linear_ms": round(l_avg, 5),
+                "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
+                "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            }
+        del strips
+
         # The prompt path against the decode linear on a 128-row prompt (fewer steps: ~2 ms each).
         import numpy as np
 

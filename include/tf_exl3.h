@@ -113,6 +113,31 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
                    int waves, void* stream);
 
 /*
+ * linear_strips: tf_exl3_linear on a stream in the strips layout (TensorFold
+ * pull request "hip exl3: the input rotation and trellis linear for decode
+ * rows", "Checks on this head": the linear runs on the checkpoint's tile layout
+ * and on a strips layout). The strips layout holds the same tiles ordered strip
+ * by strip: tile (kt, nt) starts at word ((nt / 8) * in_dim/16 + kt) * 8 + nt % 8,
+ * times 8*bits, so each 128-column strip is one contiguous stream of
+ * in_dim/16 * 256*bits bytes. Same arguments, refusals, waves and summation
+ * order as tf_exl3_linear; for a stream and its tf_exl3_repack_strips image the
+ * outputs are bit-identical.
+ */
+int tf_exl3_linear_strips(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                          const uint32_t* strips, const uint16_t* svh, void* y, int y_dtype,
+                          int waves, void* stream);
+
+/*
+ * repack_strips: writes the strips-layout image of a tile-layout stream
+ * (tf_exl3_trellis_bytes(bits, in_dim, out_dim) bytes each; both device, 16-byte
+ * aligned, not overlapping; asynchronous on `stream`). Refusals: TF_E_BITS,
+ * TF_E_SHAPE, TF_E_NULL, TF_E_ALIGN, TF_E_ALIAS (the buffers overlap; the repack
+ * is not in place), TF_E_LAUNCH.
+ */
+int tf_exl3_repack_strips(int bits, int in_dim, int out_dim, const uint32_t* tiles, uint32_t* strips,
+                          void* stream);
+
+/*
  * linear_prompt: the prompt path, bit-equal to tf_exl3_linear (TensorFold pull
  * request "hip exl3: the input rotation and trellis linear for decode rows",
  * "Known limits": the prompt path that follows the decode rows is to give the

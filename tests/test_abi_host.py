@@ -86,7 +86,8 @@ def test_plan_refusals(lib, args, code):
 FAKE = 0x7F0000000000  # never dereferenced: every call below is refused on the host
 
 
-@pytest.mark.parametrize("entry", ["tf_exl3_linear", "tf_exl3_linear_mfma", "tf_exl3_linear_prompt"])
+@pytest.mark.parametrize("entry", ["tf_exl3_linear", "tf_exl3_linear_mfma", "tf_exl3_linear_prompt",
+                                   "tf_exl3_linear_strips"])
 def test_linear_refusals(lib, entry):
     f = getattr(lib, entry)
     ok = dict(bits=4, rows=2, k=256, n=256, z=FAKE, t=FAKE + 0x100000, s=FAKE + 0x200000, y=FAKE + 0x300000,
@@ -106,6 +107,17 @@ def test_linear_refusals(lib, entry):
     assert call(y=FAKE + 0x100000 + 64) == -7  # y overlaps the trellis
     assert call(w=2) == -8
     assert call(rows=0, z=None, y=None) == 0  # nothing to do, nothing launched
+
+
+def test_repack_refusals(lib):
+    f = lib.tf_exl3_repack_strips
+    n = tq.trellis_bytes(4, 256, 256)
+    assert f(7, 256, 256, FAKE, FAKE + 0x100000, None) == -1
+    assert f(4, 256, 200, FAKE, FAKE + 0x100000, None) == -2
+    assert f(4, 256, 256, None, FAKE + 0x100000, None) == -5
+    assert f(4, 256, 256, FAKE, FAKE + 0x100004, None) == -6
+    assert f(4, 256, 256, FAKE, FAKE + n - 16, None) == -7  # overlap: not in place
+    assert f(4, 256, 256, FAKE, FAKE, None) == -7
 
 
 def test_rot_in_refusals(lib):

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     linear_plan,
     project,
     project_pass_rows,
+    repack_strips,
     load,
     rot_in,
     status_string,

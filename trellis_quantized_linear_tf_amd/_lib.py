@@ -53,6 +53,8 @@ SIGNATURES = {
     "tf_exl3_linear": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_linear_mfma": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_linear_prompt": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_linear_strips": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
+    "tf_exl3_repack_strips": (_I, [_I, _I, _I, _P, _P, _P]),
     "tf_exl3_project": (_I, [_I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_project_pass_rows": (_I, [_I, _I, _I, _I]),
     "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
@@ -158,14 +160,15 @@ def rot_in(x, suh, z=None):
     return z
 
 
-ENGINES = ("dot2", "mfma", "prompt")
+ENGINES = ("dot2", "mfma", "prompt", "strips")
 
 
 def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0,
            engine: str = "dot2"):
     """y[rows][out_dim] = the trellis linear of fp16 z [rows][in_dim] (trellis: uint8/int32 stream).
-    engine "dot2" runs tf_exl3_linear, "mfma" tf_exl3_linear_mfma and "prompt"
-    tf_exl3_linear_prompt (32-row passes, bit-equal to "dot2")."""
+    engine "dot2" runs tf_exl3_linear, "mfma" tf_exl3_linear_mfma, "prompt"
+    tf_exl3_linear_prompt (32-row passes, bit-equal to "dot2") and "strips"
+    tf_exl3_linear_strips (trellis in the strips layout, see repack_strips)."""
     torch = _torch()
     rows, in_dim = z.shape
     if y is None:
@@ -173,10 +176,20 @@ def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, wav
     if engine not in ENGINES:
         raise ValueError(f"engine must be one of {ENGINES}")
     lib = load()
-    fn = {"dot2": lib.tf_exl3_linear, "mfma": lib.tf_exl3_linear_mfma, "prompt": lib.tf_exl3_linear_prompt}[engine]
+    fn = {"dot2": lib.tf_exl3_linear, "mfma": lib.tf_exl3_linear_mfma, "prompt": lib.tf_exl3_linear_prompt,
+          "strips": lib.tf_exl3_linear_strips}[engine]
     _check(fn(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y), _dt_code(y.dtype), waves,
               _stream(z)))
     return y
+
+
+def repack_strips(trellis, bits: int, in_dim: int, out_dim: int, out=None):
+    """The strips-layout image of a tile-layout stream (tf_exl3_repack_strips)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(trellis)
+    _check(load().tf_exl3_repack_strips(bits, in_dim, out_dim, _ptr(trellis), _ptr(out), _stream(trellis)))
+    return out
 
 
 def project(x, suh, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0):

@@ -144,7 +144,30 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
   const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
   if (st != TF_OK || rows == 0) return st;
   const hipError_t e = tf_exl3::launch_linear(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
-                                              y_dtype, static_cast<hipStream_t>(stream));
+                                              y_dtype, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
+int tf_exl3_linear_strips(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* strips,
+                          const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, strips, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK || rows == 0) return st;
+  const hipError_t e = tf_exl3::launch_linear(bits, plan.waves, rows, in_dim, out_dim, z, strips, svh, y,
+                                              y_dtype, 1, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
+int tf_exl3_repack_strips(int bits, int in_dim, int out_dim, const uint32_t* tiles, uint32_t* strips,
+                          void* stream) {
+  if (width_index(bits) < 0) return TF_E_BITS;
+  const uint64_t n = stream_bytes(bits, in_dim, out_dim);
+  if (n == 0) return TF_E_SHAPE;
+  if (tiles == nullptr || strips == nullptr) return TF_E_NULL;
+  if (!aligned(tiles, 16) || !aligned(strips, 16)) return TF_E_ALIGN;
+  if (overlap(tiles, (size_t)n, strips, (size_t)n)) return TF_E_ALIAS;
+  const hipError_t e =
+      tf_exl3::launch_repack_strips(bits, in_dim, out_dim, tiles, strips, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 

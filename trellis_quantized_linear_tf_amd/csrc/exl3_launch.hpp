@@ -56,9 +56,13 @@ hipError_t launch_project(int bits, int waves, int nr_cap, int rows, int in_dim,
 hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,
                          int in_dim, hipStream_t stream);
 
+// layout: 0 = tile layout, 1 = strips layout (kLayoutTiles / kLayoutStrips).
 hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
-                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
                          hipStream_t stream);
+
+hipError_t launch_repack_strips(int bits, int in_dim, int out_dim, const uint32_t* tiles, uint32_t* strips,
+                                hipStream_t stream);
 
 // Rows per full pass of the prompt path (the rest runs as decode passes).
 constexpr int kPromptRowsPerPass = 32;

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
                                                               const uint32_t* __restrict__ trellis,
                                                               const uint16_t* __restrict__ svh,
                                                               void* __restrict__ y, int y_dtype,
-                                                              int rows, int in_dim, int out_dim) {
+                                                              int rows, int in_dim, int out_dim,
+                                                              int layout) {
   __shared__ float partial[WAVES * (NR < kRowsPerPass ? NR : kRowsPerPass) * kBlock];
 
   const int lane = __lane_id();
@@ -52,11 +53,10 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   const int nr = min(NR, rows - r0);
   const int iters = in_dim / 16 / WAVES;
 
-  // Stream words of one tile row across the whole matrix, and this lane's share
-  // of tile row kt = wave in this strip.
-  const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
-  const uint32_t* __restrict__ tp = trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS;
-  const size_t step_words = (size_t)WAVES * row_words;
+  // This strip's tile row kt = wave, and the words between the wave's tile rows.
+  const StreamStrides st = stream_strides<BITS>(layout, in_dim, out_dim);
+  const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
+  const size_t step_words = (size_t)WAVES * st.row;
   const int off = lane * BITS;
   const int nb = next_lane_in_tile(lane) * BITS;
 
@@ -158,7 +158,7 @@ struct LdsWalk {
 template <int BITS, int WAVES, int NR>
 __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_lds_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
-    void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
+    void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim, int layout) {
   __shared__ float partial[WAVES * kRowsPerPass * kBlock];
   __shared__ uint4 zslot[WAVES][2 * NR];
 
@@ -168,13 +168,13 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   const int r0 = blockIdx.y * NR;
   const int nr = min(NR, rows - r0);
   const int iters = in_dim / 16 / WAVES;
-  const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
+  const StreamStrides st = stream_strides<BITS>(layout, in_dim, out_dim);
 
   // Lane l stages row min(l / 2, nr - 1), k-half l % 2 of tile row kt = wave + i * WAVES.
   const int zr = min(lane >> 1, nr - 1);
   LdsWalk<BITS, WAVES, NR> walk{
-      trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS,
-      (size_t)WAVES * row_words,
+      trellis + (size_t)wave * st.row + (size_t)strip * st.strip,
+      (size_t)WAVES * st.row,
       lane * BITS,
       next_lane_in_tile(lane) * BITS,
       iters,
@@ -195,26 +195,26 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
 // NR <= kScalarZRows, else through LDS.
 template <int BITS, int WAVES, int NR>
 static void launch_nr(dim3 grid, const uint16_t* z, const uint32_t* trellis, const uint16_t* svh, void* y,
-                      int y_dtype, int rows, int in_dim, int out_dim, hipStream_t stream) {
+                      int y_dtype, int rows, int in_dim, int out_dim, int layout, hipStream_t stream) {
   if constexpr (NR <= kScalarZRows) {
     hipLaunchKernelGGL((linear_kernel<BITS, WAVES, NR>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh,
-                       y, y_dtype, rows, in_dim, out_dim);
+                       y, y_dtype, rows, in_dim, out_dim, layout);
   } else {
     hipLaunchKernelGGL((linear_lds_kernel<BITS, WAVES, NR>), grid, dim3(kWave * WAVES), 0, stream, z, trellis,
-                       svh, y, y_dtype, rows, in_dim, out_dim);
+                       svh, y, y_dtype, rows, in_dim, out_dim, layout);
   }
 }
 
 template <int BITS, int WAVES>
 static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
-                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
                             hipStream_t stream) {
   const int full = rows / kRowsPerPass;
   const int rest = rows % kRowsPerPass;
   const int strips = out_dim / kBlock;
   if (full > 0) {
     launch_nr<BITS, WAVES, 16>(dim3(strips, full), z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim,
-                               out_dim, stream);
+                               out_dim, layout, stream);
   }
   if (rest > 0) {
     const size_t off = (size_t)full * kRowsPerPass;
@@ -223,12 +223,12 @@ static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z
                                       : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
     const dim3 grid(strips, 1);
     switch (rows_bucket(rest)) {
-      case 1: launch_nr<BITS, WAVES, 1>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
-      case 2: launch_nr<BITS, WAVES, 2>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
-      case 4: launch_nr<BITS, WAVES, 4>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
-      case 8: launch_nr<BITS, WAVES, 8>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
-      case 12: launch_nr<BITS, WAVES, 12>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
-      default: launch_nr<BITS, WAVES, 16>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, stream); break;
+      case 1: launch_nr<BITS, WAVES, 1>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      case 2: launch_nr<BITS, WAVES, 2>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      case 4: launch_nr<BITS, WAVES, 4>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      case 8: launch_nr<BITS, WAVES, 8>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      case 12: launch_nr<BITS, WAVES, 12>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      default: launch_nr<BITS, WAVES, 16>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
     }
   }
   return hipGetLastError();
@@ -236,23 +236,23 @@ static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z
 
 template <int BITS>
 static hipError_t launch_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
-                           const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                           const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
                            hipStream_t stream) {
-  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
 }
 
 hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
-                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                         const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
                          hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   switch (bits) {
-    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
   }
 }
 
@@ -265,13 +265,14 @@ static hipError_t launch_prompt_bw(int rows, int in_dim, int out_dim, const uint
   if (full > 0) {
     hipLaunchKernelGGL((linear_lds_kernel<BITS, WAVES, kPromptRowsPerPass>), dim3(out_dim / kBlock, full),
                        dim3(kWave * WAVES), 0, stream, z, trellis, svh, y, y_dtype, full * kPromptRowsPerPass,
-                       in_dim, out_dim);
+                       in_dim, out_dim, kLayoutTiles);
   }
   if (rest > 0) {
     const size_t off = (size_t)full * kPromptRowsPerPass;
     void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
                                       : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
-    return launch_bw<BITS, WAVES>(rest, in_dim, out_dim, z + off * in_dim, trellis, svh, yr, y_dtype, stream);
+    return launch_bw<BITS, WAVES>(rest, in_dim, out_dim, z + off * in_dim, trellis, svh, yr, y_dtype,
+                                  kLayoutTiles, stream);
   }
   return hipGetLastError();
 }

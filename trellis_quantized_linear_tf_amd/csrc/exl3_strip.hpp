@@ -11,6 +11,25 @@
 
 namespace tf_exl3 {
 
+// Stream layouts. Both store a strip's tile row (its 8 tiles, 64 * BITS words)
+// contiguously; the tile layout puts whole tile rows (every strip) one after
+// another, the strips layout puts each strip's tile rows together, so a strip
+// is one contiguous stream.
+constexpr int kLayoutTiles = 0;
+constexpr int kLayoutStrips = 1;
+
+struct StreamStrides {
+  size_t row;    // words from a strip's tile row kt to kt + 1
+  size_t strip;  // words from strip s's tile row kt to strip s + 1's
+};
+
+template <int BITS>
+__device__ __forceinline__ StreamStrides stream_strides(int layout, int in_dim, int out_dim) {
+  const size_t unit = 64 * BITS;
+  if (layout == kLayoutStrips) return {unit, (size_t)(in_dim / 16) * unit};
+  return {(size_t)(out_dim / 128) * unit, unit};
+}
+
 // Tile rows in flight per wave: about 4 KiB of stream per wave.
 template <int BITS>
 constexpr int prefetch_depth() {
