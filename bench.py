@@ -37,7 +37,7 @@ KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_
                   "exl3_project.hip"]
 PROMPT_ROWS = 128
 # (engine, rows) regions whose HBM counters ingest_counters reads.
-COUNTER_REGIONS = [("dot2", 1), ("dot2", 16), ("mfma", 1), ("mfma", 16), ("fused", 1)]
+COUNTER_REGIONS = [("dot2", 1), ("dot2", 16), ("mfma", 1), ("mfma", 16), ("fused", 1), ("strips", 1)]
 
 
 def _bucket(rows: int) -> int:
