@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -59,10 +60,19 @@ def kernel_name(engine: str, rows: int) -> str:
 PROMPT_ROWS = 128
 
 
-def kernel_source_hash() -> str:
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace collapsed (the kernels' code only)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the kernels' code (comments and layout ignored), keying the traffic record."""
+    read = read or (lambda name: (ROOT / "trellis_quantized_linear_tf_amd" / "csrc" / name).read_text())
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        h.update((ROOT / "trellis_quantized_linear_tf_amd" / "csrc" / name).read_bytes())
+        h.update(code_text(read(name)).encode())
     return h.hexdigest()[:16]
 
 

@@ -115,8 +115,8 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
 /*
  * linear_strips: tf_exl3_linear on a stream in the strips layout (TensorFold
  * pull request "hip exl3: the input rotation and trellis linear for decode
- * rows", "Checks on this head": the linear runs on the checkpoint's tile layout
- * and on a strips layout). The strips layout holds the same tiles ordered strip
+ * rows", "Checks on this head": the identity check runs on the checkpoint's tile
+ * layout at 4 waves and on a strips layout at 8). The strips layout holds the same tiles ordered strip
  * by strip: tile (kt, nt) starts at word ((nt / 8) * in_dim/16 + kt) * 8 + nt % 8,
  * times 8*bits, so each 128-column strip is one contiguous stream of
  * in_dim/16 * 256*bits bytes. Same arguments, refusals, waves and summation

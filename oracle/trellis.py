@@ -20,8 +20,9 @@ or value order, so this module fixes one concrete format (readings, in order):
      pairs are adjacent values.
   R4 tile order: tile (kt, nt) of an in_dim x out_dim matrix starts at word
      (kt * out_dim/16 + nt) * 8K (row-major tiles, the "tile layout").
-  R21 strips layout (the same section's identity test runs "at 8 waves on the
-     strips layout" without defining it): the same tiles, ordered so that each
+  R21 strips layout (the identity test of "Checks on this head" also runs on a
+     layout it calls the strips layout, at 8 waves, and does not define it):
+     the same tiles, ordered so that each
      128-column strip (8 tile columns) is one contiguous stream: tile (kt, nt)
      starts at word ((nt div 8) * in_dim/16 + kt) * 8 + nt mod 8, times 8K.
   R5 codebook: x = (state * 0x9E3779) mod 2^32 (a 24-bit Fibonacci-hashing

@@ -1,7 +1,7 @@
 """The prompt path (tf_exl3_linear_prompt) on the GPU.
 
 Its rows must be bit-identical to the decode linear's (the page's "Known limits":
-the prompt path is registered bit-equal to this linear), for every width, both
+the prompt path that follows must reproduce the decode linear's bits), for every width, both
 wave counts, the three output types and row counts on both sides of the 32-row
 pass (a remainder that runs as decode passes). The oracle's gate is checked on
 one case directly, and on sampled strips at the LM-head shape.

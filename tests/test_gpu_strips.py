@@ -1,7 +1,7 @@
 """The strips layout on the GPU: the repacker against the oracle's layout, bit for bit,
 and tf_exl3_linear_strips against tf_exl3_linear on the same tiles, bit for bit (same
-waves, same order), including the page's identity check at 8 waves on the strips layout
-("Checks on this head") and the LM-head shape."""
+waves, same order), including the page's identity check run at 8 waves on the strips
+layout ("Checks on this head") and the LM-head shape."""
 
 import numpy as np
 import pytest

@@ -29,8 +29,8 @@
 // p = 0..7 in ascending k; it is the same in every variant, whichever way z
 // arrives, so a row's bits never depend on the variant.
 //
-// Prompt path (the same page, "Known limits": prompt rows must come out
-// bit-equal to this linear): full passes of 32 rows decode each tile row once
+// Prompt path (the same page, "Known limits": the prompt path that follows must
+// reproduce the decode linear's bits): full passes of 32 rows decode each tile row once
 // for twice the rows; the remainder runs as decode passes.
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
