@@ -6,6 +6,8 @@
 // svh follow the finish of the reference path.
 #pragma once
 
+#include <type_traits>
+
 #include "exl3_device.hpp"
 #include "tf_exl3.h"
 
@@ -110,6 +112,23 @@ struct StreamWalk {
     }
   }
 };
+
+// Runs step(slot, i) for i = 0 .. iters - 1, where slot = i % RING arrives as a
+// std::integral_constant, so register rings indexed by it stay in registers.
+template <int D, int RING, class F>
+__device__ __forceinline__ void steps_from(F& step, int it, int iters, bool tail) {
+  if constexpr (D < RING) {
+    if (!tail || it + D < iters) step(std::integral_constant<int, D>{}, it + D);
+    steps_from<D + 1, RING>(step, it, iters, tail);
+  }
+}
+
+template <int RING, class F>
+__device__ __forceinline__ void step_loop(int iters, F& step) {
+  int it = 0;
+  for (; it + RING <= iters; it += RING) steps_from<0, RING>(step, it, iters, false);
+  steps_from<0, RING>(step, it, iters, true);
+}
 
 __device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, size_t i, float v) {
   if (y_dtype == TF_DT_F32) {
