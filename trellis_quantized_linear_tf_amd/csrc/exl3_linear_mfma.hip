@@ -50,19 +50,12 @@ __device__ __forceinline__ half8_t pairs_to_half8(half2_t a, half2_t b, half2_t 
   return __builtin_bit_cast(half8_t, u);
 }
 
-// Waves per SIMD the register budget aims at.
-template <int NG>
-constexpr int mfma_waves_per_simd() {
-  return NG == 4 ? 4 : 5;
-}
-
-// Passes of up to 4 rows (NG = 1 group of four), or any multiple of 4 up to 16
-// (NG = 2, 4), on v_mfma_f32_16x16x32_f16.
-template <int BITS, int WAVES, int NG>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<NG>()))) void linear_mfma_kernel(
+// Passes of up to 4 rows on v_mfma_f32_16x16x32_f16.
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(5))) void linear_mfma_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
-  constexpr int NR = 4 * NG;
+  constexpr int NR = 4;
   constexpr int PF = prefetch_depth<BITS>();
   constexpr int RING = PF + 1;
   __shared__ float partial[WAVES * NR * kBlock];
@@ -71,8 +64,7 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(mf
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int strip = blockIdx.x;
-  const int r0 = blockIdx.y * NR;
-  const int nr = min(NR, rows - r0);
+  const int nr = min(NR, rows);
   const int iters = in_dim / 16 / WAVES;
 
   const StreamStrides st = stream_strides<BITS>(kLayoutTiles, in_dim, out_dim);
@@ -82,26 +74,22 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(mf
   const int nb = next_lane_in_tile(lane) * BITS;
   auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
 
-  // z staging: lane l < 2 * NR loads row min(l / 2, nr - 1), k-half l % 2.
+  // z staging: lane l < 8 loads row min(l / 2, nr - 1), k-half l % 2.
   const bool stager = lane < 2 * NR;
   const uint4* __restrict__ zsrc = reinterpret_cast<const uint4*>(
-      z + (size_t)(r0 + min(lane >> 1, nr - 1)) * in_dim + wave * 16 + (lane & 1) * 8);
+      z + (size_t)min(lane >> 1, nr - 1) * in_dim + wave * 16 + (lane & 1) * 8);
   auto zload = [&](int i) { return zsrc[(size_t)min(i, iters - 1) * (WAVES * 2)]; };
   if (lane == 0) zslot[wave][2 * NR] = make_uint4(0u, 0u, 0u, 0u);
 
-  // A addresses: lane 16G + m reads row 4j + m / 4 (clamped) iff m % 4 == G.
+  // A address: lane 16G + m reads row min(m / 4, nr - 1) iff m % 4 == G.
   const int m = lane & 15;
   const bool part = (m & 3) == (lane >> 4);
-  int abase[NG];
-#pragma unroll
-  for (int j = 0; j < NG; ++j) abase[j] = part ? 2 * min(4 * j + (m >> 2), nr - 1) : 2 * NR;
+  const int abase = part ? 2 * min(m >> 2, nr - 1) : 2 * NR;
   const int aq = part ? 1 : 0;
 
-  f32x4 acc[NG][2];
+  f32x4 acc[2];
 #pragma unroll
-  for (int j = 0; j < NG; ++j)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) acc[j][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < 2; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   uint32_t ring[RING][BITS + 1];
   uint4 zn = zload(0);
@@ -117,39 +105,31 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(mf
     half2_t wp[2][8];
     decode_lane<BITS>(ring[D], wp);
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
+    for (int q = 0; q < 2; ++q) {
+      const half8_t a = __builtin_bit_cast(half8_t, zslot[wave][abase + q * aq]);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const half8_t a = __builtin_bit_cast(half8_t, zslot[wave][abase[j] + q * aq]);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const half8_t b =
-              pairs_to_half8(wp[c][4 * q], wp[c][4 * q + 1], wp[c][4 * q + 2], wp[c][4 * q + 3]);
-          acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j][c], 0, 0, 0);
-        }
+      for (int c = 0; c < 2; ++c) {
+        const half8_t b = pairs_to_half8(wp[c][4 * q], wp[c][4 * q + 1], wp[c][4 * q + 2], wp[c][4 * q + 3]);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
       }
     }
   };
   step_loop<RING>(iters, step);
 
-  // D entry i of acc[j][c]: pass row 4j + G, strip column 32i + 2n + c.
+  // D entry i of acc[c]: pass row G, strip column 32i + 2n + c.
   const int n = lane & 15;
-  const int g = lane >> 4;
+  const int r = lane >> 4;
+  if (r < nr) {
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const int r = 4 * j + g;
-    if (r < nr) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float2 v;
-        v.x = acc[j][0][i];
-        v.y = acc[j][1][i];
-        *reinterpret_cast<float2*>(&partial[(wave * NR + r) * kBlock + 32 * i + 2 * n]) = v;
-      }
+    for (int i = 0; i < 4; ++i) {
+      float2 v;
+      v.x = acc[0][i];
+      v.y = acc[1][i];
+      *reinterpret_cast<float2*>(&partial[(wave * NR + r) * kBlock + 32 * i + 2 * n]) = v;
     }
   }
   __syncthreads();
-  finish_strip<WAVES>(partial, NR, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
+  finish_strip<WAVES>(partial, NR, wave, lane, nr, 0, strip, out_dim, svh, y, y_dtype);
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -264,11 +244,11 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
-template <int BITS, int WAVES, int NG>
-static void launch_g(dim3 grid, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
+template <int BITS, int WAVES>
+static void launch_4(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
                      const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES, NG>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh,
-                     y, y_dtype, rows, in_dim, out_dim);
+  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES>), dim3(out_dim / kBlock), dim3(kWave * WAVES), 0, stream, z,
+                     trellis, svh, y, y_dtype, rows, in_dim, out_dim);
 }
 
 template <int BITS, int WAVES>
@@ -294,7 +274,7 @@ static hipError_t launch_mfma_bw(int rows, int in_dim, int out_dim, const uint16
                                       : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
     const dim3 grid(strips, 1);
     if (rest <= 4) {
-      launch_g<BITS, WAVES, 1>(grid, rest, in_dim, out_dim, zr, trellis, svh, yr, y_dtype, stream);
+      launch_4<BITS, WAVES>(rest, in_dim, out_dim, zr, trellis, svh, yr, y_dtype, stream);
     } else {
       launch_32<BITS, WAVES>(grid, rest, in_dim, out_dim, zr, trellis, svh, yr, y_dtype, stream);
     }
