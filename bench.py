@@ -34,8 +34,15 @@ WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
 CPU_SAMPLE_STRIPS = 128
 WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
-KERNEL_SOURCES = ["exl3_device.hpp", "exl3_strip.hpp", "exl3_linear.hip", "exl3_linear_mfma.hip",
-                  "exl3_project.hip"]
+# The sources each engine's linear kernel is built from (the traffic record is keyed on them).
+_COMMON = ["exl3_device.hpp", "exl3_strip.hpp"]
+ENGINE_SOURCES = {
+    "dot2": _COMMON + ["exl3_linear.hip"],
+    "strips": _COMMON + ["exl3_linear.hip"],
+    "prompt": _COMMON + ["exl3_linear.hip"],
+    "mfma": _COMMON + ["exl3_linear_mfma.hip"],
+    "fused": _COMMON + ["exl3_project.hip"],
+}
 PROMPT_ROWS = 128
 # (engine, rows) regions whose HBM counters ingest_counters reads.
 COUNTER_REGIONS = [("dot2", 1), ("dot2", 16), ("mfma", 1), ("mfma", 16), ("fused", 1), ("strips", 1)]
@@ -67,11 +74,11 @@ def code_text(src: str) -> str:
     return " ".join(src.split())
 
 
-def kernel_source_hash(read=None) -> str:
-    """Hash of the kernels' code (comments and layout ignored), keying the traffic record."""
+def kernel_source_hash(engine: str, read=None) -> str:
+    """Hash of an engine's kernel code (comments and layout ignored), keying its traffic record."""
     read = read or (lambda name: (ROOT / "trellis_quantized_linear_tf_amd" / "csrc" / name).read_text())
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in ENGINE_SOURCES[engine]:
         h.update(code_text(read(name)).encode())
     return h.hexdigest()[:16]
 
@@ -86,13 +93,14 @@ def algorithmic_bytes(rows: int) -> dict:
 
 
 def load_traffic(engine: str, rows: int):
-    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    """Counter-measured HBM bytes per launch, if taken on the engine's current kernel code."""
     if not TRAFFIC_FILE.exists():
         return None
     rec = json.loads(TRAFFIC_FILE.read_text())
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    key = f"{engine}:{rows}"
+    if rec.get("code_hash", {}).get(key) != kernel_source_hash(engine):
         return None
-    return rec.get("per_launch_bytes", {}).get(f"{engine}:{rows}")
+    return rec.get("per_launch_bytes", {}).get(key)
 
 
 def make_inputs(torch, dev, rows: int, copies: int):
@@ -113,17 +121,29 @@ def make_inputs(torch, dev, rows: int, copies: int):
 
 
 def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, engine: str = "dot2"):
-    """Warm up, then time exactly `steps` steps; HIP events around every linear launch."""
+    """Warm up, then two timed regions of exactly `steps` steps each: the steps alone
+    (events only before and after: ms per step), then the same steps with HIP events
+    around every launch of the linear's kernel, on its stream (its duration: the
+    events themselves cost the step a few microseconds, so they stay out of the first
+    region)."""
     rows = xt.shape[0]
     z = torch.empty((rows, IN_DIM), dtype=torch.float16, device=xt.device)
     y = torch.empty((rows, OUT_DIM), dtype=torch.float32, device=xt.device)
     copies = len(trellis)
-    def step(i):
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
         if engine == "fused":
+            if ev:
+                ev[0].record(stream)
             tq.project(xt, suh_t, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
         else:
             tq.rot_in(xt, suh_t, z)
+            if ev:
+                ev[0].record(stream)
             tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+        if ev:
+            ev[1].record(stream)
 
     # At least `warmup` steps and at least WARMUP_S seconds, so clocks settle first.
     t_start = time.perf_counter()
@@ -133,26 +153,22 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, en
         i += 1
         if i % 64 == 0:
             torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
-        if engine == "fused":
-            ev[i][0].record(stream)
-            tq.project(xt, suh_t, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
-        else:
-            tq.rot_in(xt, suh_t, z)
-            ev[i][0].record(stream)
-            tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
-        ev[i][1].record(stream)
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
     lin_ms = [a.elapsed_time(b) for a, b in ev]
     return total_ms, lin_ms, wall, y
 
@@ -256,7 +272,7 @@ def ingest_counters(base: Path) -> dict:
             raw[f"{engine}:{rows}"] = {"FETCH_SIZE": fetch, "WRITE_SIZE": write}
             per[f"{engine}:{rows}"] = int(round(fetch * 1024 * f_read + write * 1024 * f_write))
     rec = {
-        "kernel_source_hash": kernel_source_hash(),
+        "code_hash": {k: kernel_source_hash(k.split(":")[0]) for k in per},
         "copy_kib_per_launch": {"FETCH_SIZE": copy_fetch, "WRITE_SIZE": copy_write},
         "scale": {"read": f_read, "write": f_write},
         "linear_kib_per_launch": raw,
