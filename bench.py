@@ -284,6 +284,67 @@ def ingest_counters(base: Path) -> dict:
     return rec
 
 
+# The test suite's workloads (shape, widths, rows, input and output types, waves).
+CONFIGS = [
+    ("indexer wk 512->128", 1, 512, 128, (4,), (1,), "f16", "f32", 0),
+    ("Engram wkv 6144->25600", 2, 6144, 25600, (3, 4), (1, 2, 8, 16), "bf16", "f16", 4),
+    ("LM head 5120->129280", 3, 5120, 129280, (4,), (1, 16), "f16", "f32", 0),
+    ("width sweep 6144->25600", 4, 6144, 25600, (2, 3, 4, 5, 6, 8), (64,), "f16", "f32", 8),
+    ("stress LM head 8-bit", 5, 5120, 129280, (8,), (64,), "bf16", "f32", 0),
+]
+
+
+def time_configs(torch, tq, steps: int) -> list:
+    """Step time (rot_in + linear) of every workload, both engines, HIP events around
+    the steps only (one stream copy: these shapes' streams are not all larger than the
+    Infinity Cache, so the small ones may run from it)."""
+    import numpy as np
+
+    import synth
+
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    out = []
+    for name, wid, k, n, widths, row_counts, xdt, ydt, waves in CONFIGS:
+        suh = torch.from_numpy(synth.signs(synth.seed_for(wid, synth.STREAM_SUH), k).view(np.int16)).to(dev)
+        svh = torch.from_numpy(synth.signs(synth.seed_for(wid, synth.STREAM_SVH), n).view(np.int16)).to(dev)
+        for bits in widths:
+            stream = synth.trellis_words(synth.seed_for(wid, synth.STREAM_TRELLIS), bits, k, n)
+            tt = torch.from_numpy(stream.view(np.int32)).to(dev)
+            for rows in row_counts:
+                x = synth.rows(synth.seed_for(wid, synth.STREAM_ROWS), rows, k, xdt, 1.0)
+                xt = torch.from_numpy(x.view(np.int16 if xdt != "f32" else np.float32)).to(dev)
+                if xdt != "f32":
+                    xt = xt.view(tdt[xdt])
+                z = torch.empty((rows, k), dtype=torch.float16, device=dev)
+                y = torch.empty((rows, n), dtype=tdt[ydt], device=dev)
+                rec = {"workload": name, "bits": bits, "rows": rows, "x": xdt, "y": ydt,
+                       "waves": tq.linear_plan(bits, rows, k, n, waves)["waves"]}
+                for engine in ("dot2", "mfma"):
+                    def step():
+                        tq.rot_in(xt, suh, z)
+                        tq.linear(z, tt, svh, bits, n, y=y, waves=waves, engine=engine)
+
+                    t_start = time.perf_counter()
+                    while time.perf_counter() - t_start < 0.2:
+                        step()
+                    torch.cuda.synchronize()
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(steps):
+                        step()
+                    b.record()
+                    torch.cuda.synchronize()
+                    us = a.elapsed_time(b) / steps * 1e3
+                    rec[f"{engine}_us"] = round(us, 2)
+                    rec[f"{engine}_stream_gbps"] = round(k * n * bits / 8 / (us * 1e-6) / 1e9, 1)
+                    rec[f"{engine}_rows_per_s"] = round(rows / (us * 1e-6), 1)
+                out.append(rec)
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +360,8 @@ def main() -> int:
     ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
     ap.add_argument("--ingest-counters", metavar="DIR", help="write the traffic record from --pmc runs in DIR")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload of the test suite (both engines) and print one JSON line")
     args = ap.parse_args()
 
     if args.ingest_counters:
@@ -323,6 +386,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, tq, dev, args.steps)
+        return 0
+    if args.configs:
+        print(json.dumps({"configs": time_configs(torch, tq, max(10, args.steps // 4))}))
         return 0
 
     rows = args.rows
