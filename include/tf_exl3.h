@@ -194,10 +194,14 @@ typedef struct {
   int grid_x;         /* blocks per pass = out_dim / 128 */
   int passes;         /* ceil(rows / 16) */
   int rows_last_pass; /* rows in the last pass (1..16), 0 when rows == 0 */
-  int rows_kernel;    /* row capacity of the variant for the first pass: 1, 2, 4, 8, 12 or 16
+  int rows_kernel;    /* row capacity of the variant for the first launch: 1, 2, 4, 8, 12 or 16
                          (up to 4 rows z arrives through scalar loads, above through LDS) */
-  int lds_bytes;      /* LDS per block of that pass: partial sums waves * min(rows_kernel, 16)
-                         * 512 bytes, plus z slots waves * 2 * rows_kernel * 16 bytes above 4 rows */
+  int lds_bytes;      /* LDS per block of that launch: partial sums waves * min(rows_kernel, 16)
+                         * 512 bytes, plus z slots (w * 2 * rows_kernel * 16 bytes, w = the block's
+                         waves) above 4 rows or when column_split */
+  int column_split;   /* 1 if that launch runs the column-split variant: a launch with fewer than
+                         2048 waves in flight gets twice the waves per block (threads = 128 *
+                         waves), each lane one column, with the same sums in the same order */
 } tf_exl3_plan;
 
 /* Fills *out with the plan for these arguments, or returns the refusal the linear
@@ -220,6 +224,12 @@ const char* tf_exl3_status_string(int status);
  *   a tile-layout stream through the linear's own load, window and codebook path.
  */
 int tf_exl3_debug_decode_states(const uint16_t* states, uint16_t* w, int n, void* stream);
+/* debug_linear_split: tf_exl3_linear with the variant forced for every launch
+ * (split 0: the regular kernels, 1: the column-split ones), so the two can be
+ * compared bit for bit on the same shape; split outside {0, 1} is TF_E_SHAPE. */
+int tf_exl3_debug_linear_split(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                               const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
+                               int waves, int split, void* stream);
 int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
                                uint16_t* w, void* stream);
 

@@ -59,15 +59,22 @@ def test_plan_fields(lib):
     p = tq.linear_plan(4, 16, 5120, 129280)
     assert p == {"width_index": 2, "waves": 8, "threads": 512, "grid_x": 1010, "passes": 1,
                  "rows_last_pass": 16, "rows_kernel": 16,
-                 "lds_bytes": 8 * 16 * 128 * 4 + 8 * 32 * 16}
+                 "lds_bytes": 8 * 16 * 128 * 4 + 8 * 32 * 16, "column_split": 0}
     p = tq.linear_plan(2, 64, 6144, 25600, waves=4)
     assert (p["waves"], p["passes"], p["rows_last_pass"]) == (4, 4, 16)
     p = tq.linear_plan(6, 17, 256, 256)
     assert (p["passes"], p["rows_last_pass"], p["rows_kernel"]) == (2, 1, 16)
-    p = tq.linear_plan(3, 3, 256, 256)
-    assert (p["passes"], p["rows_kernel"], p["lds_bytes"]) == (1, 4, 4 * 4 * 128 * 4)
+    p = tq.linear_plan(3, 3, 256, 256)  # 2 strips x 4 waves: column-split, 8 waves a block
+    assert (p["passes"], p["rows_kernel"], p["column_split"], p["threads"]) == (1, 4, 1, 512)
+    assert p["lds_bytes"] == 4 * 4 * 128 * 4 + 8 * 8 * 16
     p = tq.linear_plan(3, 10, 256, 256)
-    assert (p["passes"], p["rows_kernel"], p["lds_bytes"]) == (1, 12, 4 * 12 * 128 * 4 + 4 * 24 * 16)
+    assert (p["passes"], p["rows_kernel"], p["lds_bytes"]) == (1, 12, 4 * 12 * 128 * 4 + 8 * 24 * 16)
+    # Engram (200 strips at 4 waves: 800 waves) splits; the LM head (1010 x 8) does not,
+    # nor does a 64-row width sweep's first launch (4 passes x 200 strips x 8 waves).
+    assert tq.linear_plan(3, 1, 6144, 25600, waves=4)["column_split"] == 1
+    assert tq.linear_plan(4, 1, 5120, 129280)["column_split"] == 0
+    assert tq.linear_plan(4, 64, 6144, 25600, waves=8)["column_split"] == 0
+    assert tq.linear_plan(4, 16, 6144, 25600, waves=8)["column_split"] == 1
     assert tq.linear_plan(5, 0, 128, 128)["passes"] == 0
     assert [tq.linear_plan(b, 1, 128, 128)["width_index"] for b in tq.WIDTHS] == [0, 1, 2, 3, 4, 5]
 

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     calib_copy,
     calib_stream_read,
     debug_decode_tiles,
+    debug_linear_split,
     header_functions,
     linear,
     linear_plan,

@@ -40,6 +40,7 @@ class Plan(ctypes.Structure):
         ("rows_last_pass", ctypes.c_int),
         ("rows_kernel", ctypes.c_int),
         ("lds_bytes", ctypes.c_int),
+        ("column_split", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:
@@ -55,6 +56,7 @@ SIGNATURES = {
     "tf_exl3_linear_prompt": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_linear_strips": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_repack_strips": (_I, [_I, _I, _I, _P, _P, _P]),
+    "tf_exl3_debug_linear_split": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
     "tf_exl3_project": (_I, [_I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_project_pass_rows": (_I, [_I, _I, _I, _I]),
     "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
@@ -224,6 +226,19 @@ def debug_decode_tiles(trellis, bits: int, in_dim: int, out_dim: int):
     w = torch.empty((in_dim, out_dim), dtype=torch.float16, device=trellis.device)
     _check(load().tf_exl3_debug_decode_tiles(bits, in_dim, out_dim, _ptr(trellis), _ptr(w), _stream(trellis)))
     return w
+
+
+def debug_linear_split(z, trellis, svh, bits: int, out_dim: int, split: int, y=None, out_dtype=None,
+                       waves: int = 0):
+    """tf_exl3_linear with every launch forced to the regular (split 0) or the
+    column-split (split 1) kernels (tf_exl3_debug_linear_split)."""
+    torch = _torch()
+    rows, in_dim = z.shape
+    if y is None:
+        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
+    _check(load().tf_exl3_debug_linear_split(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y),
+                                             _dt_code(y.dtype), waves, split, _stream(z)))
+    return y
 
 
 def calib_copy(src, dst, blocks: int = 2048):

@@ -95,7 +95,13 @@ int tf_exl3_linear_plan(int bits, int rows, int in_dim, int out_dim, int waves, 
   p.passes = (rows + kMaxRowsPerPass - 1) / kMaxRowsPerPass;
   p.rows_last_pass = rows == 0 ? 0 : rows - (p.passes - 1) * kMaxRowsPerPass;
   p.rows_kernel = rows == 0 ? 0 : tf_exl3::rows_bucket(rows >= kMaxRowsPerPass ? kMaxRowsPerPass : rows);
-  p.lds_bytes = rows == 0 ? 0 : tf_exl3::linear_lds_bytes(w, p.rows_kernel);
+  // The first launch: the full passes, or the one pass of the remaining rows.
+  const int first_passes = rows >= kMaxRowsPerPass ? rows / kMaxRowsPerPass : 1;
+  p.column_split = rows == 0 ? 0 : (tf_exl3::column_split(out_dim, first_passes, w) ? 1 : 0);
+  p.lds_bytes = rows == 0 ? 0
+                : p.column_split ? tf_exl3::linear_cs_lds_bytes(w, p.rows_kernel)
+                                 : tf_exl3::linear_lds_bytes(w, p.rows_kernel);
+  p.threads = (p.column_split ? 128 : 64) * w;
   *out = p;
   return TF_OK;
 }
@@ -145,6 +151,18 @@ int tf_exl3_linear(int bits, int rows, int in_dim, int out_dim, const uint16_t* 
   if (st != TF_OK || rows == 0) return st;
   const hipError_t e = tf_exl3::launch_linear(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
                                               y_dtype, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
+int tf_exl3_debug_linear_split(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                               const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int waves,
+                               int split, void* stream) {
+  if (split != 0 && split != 1) return TF_E_SHAPE;
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK || rows == 0) return st;
+  const hipError_t e = tf_exl3::launch_linear(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
+                                              y_dtype, 0, static_cast<hipStream_t>(stream), split);
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 

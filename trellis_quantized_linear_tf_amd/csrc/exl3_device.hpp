@@ -134,6 +134,48 @@ __device__ __forceinline__ void decode_lane(const uint32_t (&w)[BITS + 1], half2
   }
 }
 
+// One column of a tile: its 16 values' states. u[] holds the column's bits
+// starting at bit 0 (value 0's window) and the 16 - BITS bits after them; the
+// windows sit at bits j*BITS, j = 0..15 (the same funnel-pair rule as
+// lane_states when BITS divides 16).
+template <int BITS>
+constexpr int column_words() {
+  return (16 * BITS + 16 - BITS + 31) / 32;
+}
+
+template <int BITS, int I = 0>
+__device__ __forceinline__ void column_states(const uint32_t (&u)[column_words<BITS>()], uint32_t (&st)[16]) {
+  if constexpr (I < 16) {
+    constexpr int o = I * BITS;
+    constexpr int d = o >> 5;
+    constexpr int sh = o & 31;
+    if constexpr (16 % BITS == 0) {
+      if constexpr (sh < 16) {
+        uint32_t t;
+        if constexpr (sh == 0) {
+          t = u[d];
+        } else {
+          t = funnel<sh>(u[d + 1], u[d]);
+        }
+        st[I] = t & 0xFFFFu;
+        if constexpr (I + 16 / BITS < 16) st[I + 16 / BITS] = t >> 16;
+      }
+    } else {
+      st[I] = window_at<BITS>(u, I);
+    }
+    column_states<BITS, I + 1>(u, st);
+  }
+}
+
+// The column's weights as packed (k, k+1) pairs: wp[p] = (W[2p][col], W[2p+1][col]).
+template <int BITS>
+__device__ __forceinline__ void decode_column(const uint32_t (&u)[column_words<BITS>()], half2_t (&wp)[8]) {
+  uint32_t st[16];
+  column_states<BITS>(u, st);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) wp[p] = decode_pair(st[2 * p], st[2 * p + 1]);
+}
+
 // Lane that holds the dword following this lane's share inside the same tile.
 __device__ __forceinline__ int next_lane_in_tile(int lane) { return (lane & ~7) | ((lane + 1) & 7); }
 

@@ -56,10 +56,30 @@ hipError_t launch_project(int bits, int waves, int nr_cap, int rows, int in_dim,
 hipError_t launch_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z, int rows,
                          int in_dim, hipStream_t stream);
 
+// A launch of the linear with fewer than this many waves in flight runs the
+// column-split variant (twice the waves, the same bits): two waves per SIMD.
+constexpr long long kSplitBelowWaves = 2048;
+
+inline bool column_split(int out_dim, int passes, int waves) {
+  return (long long)(out_dim / 128) * passes * waves < kSplitBelowWaves;
+}
+
+// LDS bytes of one column-split block (partial sums and the z slots of 2 * waves waves).
+inline int linear_cs_lds_bytes(int waves, int rows_cap) {
+  const int fr = rows_cap < 16 ? rows_cap : 16;
+  return waves * fr * 128 * 4 + 2 * waves * 2 * rows_cap * 16;
+}
+
 // layout: 0 = tile layout, 1 = strips layout (kLayoutTiles / kLayoutStrips).
+// split: -1 = by column_split(), 0 = never, 1 = always (a test hook: both give the same bits).
 hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
-                         hipStream_t stream);
+                         hipStream_t stream, int split = -1);
+
+// One launch of the column-split variant: grid (strips, passes) of row capacity nr_cap.
+void launch_linear_cs(int bits, int waves, int nr_cap, dim3 grid, const uint16_t* z, const uint32_t* trellis,
+                      const uint16_t* svh, void* y, int y_dtype, int rows, int in_dim, int out_dim, int layout,
+                      hipStream_t stream);
 
 hipError_t launch_repack_strips(int bits, int in_dim, int out_dim, const uint32_t* tiles, uint32_t* strips,
                                 hipStream_t stream);

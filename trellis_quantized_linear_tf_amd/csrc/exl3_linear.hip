@@ -208,13 +208,20 @@ static void launch_nr(dim3 grid, const uint16_t* z, const uint32_t* trellis, con
 template <int BITS, int WAVES>
 static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z,
                             const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
-                            hipStream_t stream) {
+                            int split, hipStream_t stream) {
   const int full = rows / kRowsPerPass;
   const int rest = rows % kRowsPerPass;
   const int strips = out_dim / kBlock;
+  auto use_cs = [&](int passes) { return split < 0 ? column_split(out_dim, passes, WAVES) : split == 1; };
   if (full > 0) {
-    launch_nr<BITS, WAVES, 16>(dim3(strips, full), z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim,
-                               out_dim, layout, stream);
+    const dim3 grid(strips, full);
+    if (use_cs(full)) {
+      launch_linear_cs(BITS, WAVES, 16, grid, z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim, out_dim,
+                       layout, stream);
+    } else {
+      launch_nr<BITS, WAVES, 16>(grid, z, trellis, svh, y, y_dtype, full * kRowsPerPass, in_dim, out_dim, layout,
+                                 stream);
+    }
   }
   if (rest > 0) {
     const size_t off = (size_t)full * kRowsPerPass;
@@ -222,13 +229,18 @@ static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z
     void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
                                       : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
     const dim3 grid(strips, 1);
-    switch (rows_bucket(rest)) {
-      case 1: launch_nr<BITS, WAVES, 1>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
-      case 2: launch_nr<BITS, WAVES, 2>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
-      case 4: launch_nr<BITS, WAVES, 4>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
-      case 8: launch_nr<BITS, WAVES, 8>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
-      case 12: launch_nr<BITS, WAVES, 12>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
-      default: launch_nr<BITS, WAVES, 16>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+    const int cap = rows_bucket(rest);
+    if (use_cs(1)) {
+      launch_linear_cs(BITS, WAVES, cap, grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream);
+    } else {
+      switch (cap) {
+        case 1: launch_nr<BITS, WAVES, 1>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+        case 2: launch_nr<BITS, WAVES, 2>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+        case 4: launch_nr<BITS, WAVES, 4>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+        case 8: launch_nr<BITS, WAVES, 8>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+        case 12: launch_nr<BITS, WAVES, 12>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+        default: launch_nr<BITS, WAVES, 16>(grid, zr, trellis, svh, yr, y_dtype, rest, in_dim, out_dim, layout, stream); break;
+      }
     }
   }
   return hipGetLastError();
@@ -237,22 +249,23 @@ static hipError_t launch_bw(int rows, int in_dim, int out_dim, const uint16_t* z
 template <int BITS>
 static hipError_t launch_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                            const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
-                           hipStream_t stream) {
-  if (waves == 8) return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+                           int split, hipStream_t stream) {
+  if (waves == 8)
+    return launch_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+  return launch_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
 }
 
 hipError_t launch_linear(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                          const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int layout,
-                         hipStream_t stream) {
+                         hipStream_t stream, int split) {
   if (rows == 0) return hipSuccess;
   switch (bits) {
-    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
-    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, stream);
+    case 2: return launch_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+    case 3: return launch_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+    case 4: return launch_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+    case 5: return launch_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+    case 6: return launch_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
+    default: return launch_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, layout, split, stream);
   }
 }
 
@@ -272,7 +285,7 @@ static hipError_t launch_prompt_bw(int rows, int in_dim, int out_dim, const uint
     void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
                                       : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
     return launch_bw<BITS, WAVES>(rest, in_dim, out_dim, z + off * in_dim, trellis, svh, yr, y_dtype,
-                                  kLayoutTiles, stream);
+                                  kLayoutTiles, -1, stream);
   }
   return hipGetLastError();
 }

@@ -141,10 +141,12 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int y_dtype, siz
 }
 
 // partial[(w * rstride + r) * 128 + col] holds wave w's sum for row r of the
-// pass; after a barrier, wave w finishes rows r = w, w + WAVES, ... < nr:
+// pass; after a barrier, wave w finishes rows r = w, w + STRIDE, ... < nr:
 // the waves' sums in wave order 0..WAVES-1, the fp32 output butterflies,
 // RN32(. * s), RN32(. * svh), then the cast and store of y[r0 + r][strip cols].
-template <int WAVES>
+// STRIDE is the number of waves that share the rows (WAVES unless the workgroup
+// has more waves than partial sums per row).
+template <int WAVES, int STRIDE = WAVES>
 __device__ __forceinline__ void finish_strip(const float* partial, int rstride, int wave, int lane, int nr,
                                              int r0, int strip, int out_dim, const uint16_t* __restrict__ svh,
                                              void* __restrict__ y, int y_dtype) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ void finish_strip(const float* partial, int rstride, 
   const int col = strip * kBlock + lane;
   const float g0 = f16_bits_to_f32(svh[col]);
   const float g1 = f16_bits_to_f32(svh[col + 64]);
-  for (int r = wave; r < nr; r += WAVES) {
+  for (int r = wave; r < nr; r += STRIDE) {
     float v0 = partial[r * kBlock + lane];
     float v1 = partial[r * kBlock + lane + 64];
 #pragma unroll
