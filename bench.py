@@ -37,9 +37,9 @@ TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
 # The sources each engine's linear kernel is built from (the traffic record is keyed on them).
 _COMMON = ["exl3_device.hpp", "exl3_strip.hpp"]
 ENGINE_SOURCES = {
-    "dot2": _COMMON + ["exl3_linear.hip"],
-    "strips": _COMMON + ["exl3_linear.hip"],
-    "prompt": _COMMON + ["exl3_linear.hip"],
+    "dot2": _COMMON + ["exl3_linear.hip", "exl3_linear_cs.hip"],
+    "strips": _COMMON + ["exl3_linear.hip", "exl3_linear_cs.hip"],
+    "prompt": _COMMON + ["exl3_linear.hip", "exl3_linear_cs.hip"],
     "mfma": _COMMON + ["exl3_linear_mfma.hip"],
     "fused": _COMMON + ["exl3_project.hip"],
 }
@@ -55,7 +55,7 @@ def _bucket(rows: int) -> int:
 def kernel_name(engine: str, rows: int) -> str:
     """The kernel that does the linear's work for `rows` rows on the LM head (first pass)."""
     if engine == "mfma":
-        return f"linear_mfma_kernel<{BITS}, 8>"
+        return f"linear_mfma_kernel<{BITS}, 8>" if rows <= 4 else f"linear_mfma32_kernel<{BITS}, 8>"
     if engine == "fused":
         import trellis_quantized_linear_tf_amd as tq
 
