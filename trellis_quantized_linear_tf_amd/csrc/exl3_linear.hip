@@ -27,7 +27,9 @@
 //    (16 rows per round, so a 32-row pass keeps 64 KiB of partial sums).
 // A row's chain is: for each of its wave's tile rows in ascending kt, the pairs
 // p = 0..7 in ascending k; it is the same in every variant, whichever way z
-// arrives, so a row's bits never depend on the variant.
+// arrives, so a row's bits never depend on the variant. A launch that would put
+// fewer than 2048 waves in flight (narrow matrices) runs the column-split form
+// in exl3_linear_cs.hip instead, with the same chains.
 //
 // Prompt path (the same page, "Known limits": the prompt path that follows must
 // reproduce the decode linear's bits): full passes of 32 rows decode each tile row once
@@ -82,9 +84,10 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   finish_pass<WAVES, NR>(acc, partial, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
-// The walk of linear_lds_kernel: the stream ring of StreamWalk with PF = 2 (a 32-row
-// step is long enough that two tile rows in flight cover the stream's latency),
-// plus the wave's z slice for each step staged through a wave-private LDS slot.
+// The walk of linear_lds_kernel: the stream ring of StreamWalk with PF = 2 (a step
+// of 8 or more rows runs long enough that two tile rows in flight cover the
+// stream's latency), plus the wave's z slice for each step staged through a
+// wave-private LDS slot.
 template <int BITS, int WAVES, int NR>
 struct LdsWalk {
   static_assert(2 * NR <= kWave, "a lane stages one (row, k-half) of the step's z");
