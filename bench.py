@@ -345,6 +345,19 @@ def time_configs(torch, tq, steps: int) -> list:
     return out
 
 
+def run_env(torch) -> dict:
+    """The device and software the numbers come from."""
+    props = torch.cuda.get_device_properties(0)
+    return {
+        "device": props.name,
+        "arch": getattr(props, "gcnArchName", ""),
+        "compute_units": props.multi_processor_count,
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+        "seeds": {"workload": WORKLOAD_ID, "rule": "1000 * workload + stream"},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,6 +513,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
+        "env": run_env(torch),
         **extra,
     }
     print(json.dumps(out))

@@ -134,3 +134,21 @@ def test_nonfinite_classes_propagate():
     assert np.all(np.isnan(y[1]))  # a NaN input reaches every output through the rotation
     assert not np.isfinite(y[0]).any()
     assert np.all(np.isfinite(y[2]))
+
+
+def test_float64_reference_does_not_depend_on_threads_chunks_or_rows():
+    """The page's threaded float64 reference is bit-identical to one thread ("Checks on
+    this head"); here: one BLAS thread against the default, strips in chunks of 3
+    against 32, and each row alone against all rows at once, bit for bit."""
+    from threadpoolctl import threadpool_limits
+
+    bits, k, n, rows = 4, 1024, 1280, 5
+    stream = synth.trellis_words(71, bits, k, n)
+    z = synth.rows(72, rows, k, "f16", 1.0)
+    svh = synth.signs(73, n)
+    a = lin.linear_f64(z, stream, bits, k, n, svh)
+    with threadpool_limits(1):
+        b = lin.linear_f64(z, stream, bits, k, n, svh)
+    c = lin.linear_f64(z, stream, bits, k, n, svh, strip_chunk=3)
+    d = np.concatenate([lin.linear_f64(z[i : i + 1], stream, bits, k, n, svh) for i in range(rows)])
+    assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
