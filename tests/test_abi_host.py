@@ -145,3 +145,23 @@ def test_debug_refusals(lib):
     assert lib.tf_exl3_debug_decode_states(FAKE, FAKE, -1, None) == -2
     assert lib.tf_exl3_debug_decode_tiles(7, 128, 128, FAKE, FAKE + 0x100000, None) == -1
     assert lib.tf_exl3_debug_decode_tiles(4, 128, 120, FAKE, FAKE + 0x100000, None) == -2
+
+
+def test_header_is_c_and_a_c_program_links(lib, tmp_path):
+    """include/tf_exl3.h compiles as C11 with warnings as errors, and a C program linked
+    against the library gets the planner, sizes, strings and host refusals right."""
+    import shutil
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = _lib.PKG.parent
+    exe = tmp_path / "host_calls"
+    build = subprocess.run(
+        [cc, "-std=c11", "-Wall", "-Wextra", "-Werror", f"-I{root / 'include'}",
+         str(root / "tests" / "c_abi" / "host_calls.c"), "-o", str(exe),
+         f"-L{_lib.LIB_PATH.parent}", "-ltf_exl3", f"-Wl,-rpath,{_lib.LIB_PATH.parent}"],
+        capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0 and "c abi ok" in run.stdout, run.stderr
