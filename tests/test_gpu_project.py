@@ -81,3 +81,28 @@ def test_zero_rows_and_refusal(gpu):
     assert tq.project(x, suh, st, svh, 4, 128).shape == (0, 128)
     with pytest.raises(tq.Exl3Error):
         tq.project_pass_rows(1, 32768, 128)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_nonfinite_inputs(gpu, x_dtype):
+    """inf and NaN in x go through the rotation into z and the linear exactly as the
+    two-call path takes them: the same bits (NaNs equal to NaNs) and float64's classes."""
+    bits, k, n, rows = 4, 512, 384, 3
+    stream = synth.trellis_words(7100, bits, k, n)
+    x = synth.rows(7101, rows, k, x_dtype, 1.0)
+    suh = synth.signs(7102, k)
+    svh = synth.signs(7103, n)
+    if x_dtype == "f32":
+        x[0, 5], x[1, 200], x[2, 7] = np.inf, -np.inf, np.nan
+    else:
+        x[0, 5], x[1, 200], x[2, 7] = 0x7F80, 0xFF80, 0x7FC0
+    say(f"project non-finite x={x_dtype}")
+    xt, st, tt, vt = up(x, x_dtype), up(suh), up(stream), up(svh)
+    y = down(tq.project(xt, st, tt, vt, bits, n))
+    z = tq.rot_in(xt, st)
+    y_ref = down(tq.linear(z, tt, vt, bits, n))
+    assert same_bits(y, y_ref)
+    z_oracle = rot.rot_in(x, x_dtype, suh)
+    y64 = lin.linear_f64(z_oracle, stream, bits, k, n, svh)
+    assert np.array_equal(lin.classes(y), lin.classes(y64))
+    assert np.count_nonzero(lin.classes(y)) >= 3 * 128

@@ -79,3 +79,17 @@ def test_zero_rows(gpu):
     stream, z, svh = make(4, 128, 128, 0, 980)
     say("prompt zero rows")
     assert linear(z, stream, svh, 4, 128, engine="prompt").shape == (0, 128)
+
+
+def test_nonfinite_rows(gpu):
+    """inf and NaN in some rows of a 40-row prompt: the same bits as the decode linear
+    (NaNs equal to NaNs), row by row."""
+    bits, k, n, rows = 4, 512, 384, 40
+    stream, z, svh = make(bits, k, n, rows, 990)
+    z[0, 3], z[17, 100], z[33, 7] = 0x7C00, 0xFC00, 0x7E00
+    say("prompt non-finite")
+    tt = up(stream)
+    a = linear(z, None, svh, bits, n, "f32", stream_t=tt, engine="prompt")
+    b = linear(z, None, svh, bits, n, "f32", stream_t=tt, engine="dot2")
+    assert same_bits(a, b)
+    assert np.count_nonzero(lin.classes(a)) >= 3 * 128

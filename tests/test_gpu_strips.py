@@ -91,3 +91,17 @@ def test_lm_head_strips(gpu, rows):
     a = linear(z, None, svh, bits, n, "f32", stream_t=st, engine="strips")
     b = linear(z, None, svh, bits, n, "f32", stream_t=tt, engine="dot2")
     assert same_bits(a, b)
+
+
+def test_nonfinite_on_strips(gpu):
+    bits, k, n, rows = 5, 256, 640, 3
+    stream = synth.trellis_words(4500, bits, k, n)
+    z = synth.rows(4501, rows, k, "f16", 1.0)
+    z[0, 9], z[1, 77], z[2, 200] = 0x7C00, 0xFC00, 0x7E00
+    svh = synth.signs(4502, n)
+    say("strips non-finite")
+    tt = up(stream)
+    a = linear(z, None, svh, bits, n, "f32", stream_t=repack(stream, bits, k, n), engine="strips")
+    b = linear(z, None, svh, bits, n, "f32", stream_t=tt, engine="dot2")
+    assert same_bits(a, b)
+    assert np.array_equal(lin.classes(a), lin.classes(lin.linear_f64(z, stream, bits, k, n, svh)))
