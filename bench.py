@@ -31,7 +31,7 @@ METRIC = "weight-stream GB/s and rows/s per MI355X (LM head 5120→129280, 4-bit
 HBM_PEAK_GBPS = 8000.0
 BITS, IN_DIM, OUT_DIM = 4, 5120, 129280
 WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
-CPU_SAMPLE_STRIPS = 128
+CPU_SAMPLE_STRIPS = 384  # about 10-15 s of oracle work on one core
 WARMUP_S = 0.5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
 # The sources each engine's linear kernel is built from (the traffic record is keyed on them).
@@ -199,7 +199,7 @@ def cpu_baseline(host_inputs, rows: int) -> dict:
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{rows} row, {CPU_SAMPLE_STRIPS} of 1010 strips (5120 x 16384 weights), "
+        "sample": f"{rows} row, {CPU_SAMPLE_STRIPS} of 1010 strips ({IN_DIM} x {128 * CPU_SAMPLE_STRIPS} weights), "
                   f"rot_in + float64 linear, {dt:.1f} s",
         "rows_per_s": round(rows * CPU_SAMPLE_STRIPS / 1010 / dt, 6),
     }
