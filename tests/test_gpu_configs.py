@@ -130,3 +130,34 @@ def test_whole_projection_from_x(gpu):
 
     ref = lin.dense_from_x(x, "f32", suh, tr.unpack(stream, bits, k, n), svh)
     assert np.max(np.abs(down(y) - ref)) / np.sqrt(np.mean(ref ** 2)) < 1e-2
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+def test_width_sweep_bit_equal_paths(gpu, bits):
+    """The width sweep's 64 rows through the prompt path, the strips layout and the
+    single launch: bit for bit the decode linear's outputs, at full size."""
+    k, n, rows = 6144, 25600, 64
+    stream, x, suh, svh = inputs(4, bits, k, n, rows, "f16")
+    say(f"width sweep {bits}-bit: prompt, strips and single launch against the linear")
+    tt, xt, st, vt = up(stream), up(x), up(suh), up(svh)
+    z = tq.rot_in(xt, st)
+    y = down(tq.linear(z, tt, vt, bits, n, waves=8))
+    assert same_bits(down(tq.linear(z, tt, vt, bits, n, waves=8, engine="prompt")), y)
+    strips = tq.repack_strips(tt, bits, k, n)
+    assert same_bits(down(tq.linear(z, strips, vt, bits, n, waves=8, engine="strips")), y)
+    del strips
+    assert same_bits(down(tq.project(xt, st, tt, vt, bits, n, waves=8)), y)
+
+
+def test_stress_bit_equal_paths(gpu):
+    """The stress workload's heavy-tailed fp32 rows (8-bit LM head) through the prompt
+    path and the single launch: bit for bit the decode linear's outputs."""
+    bits, k, n = 8, 5120, 129280
+    stream, _, suh, svh = inputs(5, bits, k, n, 64, "bf16")
+    xf = synth.heavy_rows(synth.seed_for(5, synth.STREAM_EXTRA), 64, k)
+    say("stress 8-bit heavy fp32 rows: prompt and single launch against the linear")
+    tt, xt, st, vt = up(stream), up(xf), up(suh), up(svh)
+    z = tq.rot_in(xt, st)
+    y = down(tq.linear(z, tt, vt, bits, n))
+    assert same_bits(down(tq.linear(z, tt, vt, bits, n, engine="prompt")), y)
+    assert same_bits(down(tq.project(xt, st, tt, vt, bits, n)), y)
