@@ -88,7 +88,8 @@ __device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo) {
   return r;
 }
 
-// The 32 states of a lane's share (see decode_lane). When BITS divides 16 the
+// The 32 states of a lane's share (see decode_lane); w[BITS] is the next
+// lane's first dword. When BITS divides 16 the
 // window at offset o + 16 is the top half of the funnel shift that gives the
 // window at o, so one shift serves two states; the 16-bit halves then reach
 // v_mul_u32_u24 through its WORD_0 / WORD_1 operand selects at no cost.
@@ -116,17 +117,32 @@ __device__ __forceinline__ void lane_states(const uint32_t (&w)[BITS + 1], uint3
   }
 }
 
+// Lane that holds the dword following this lane's share inside the same tile.
+__device__ __forceinline__ int next_lane_in_tile(int lane) { return (lane & ~7) | ((lane + 1) & 7); }
+
+// `v` of lane next_lane_in_tile(this lane), through the LDS crossbar (no LDS
+// memory is touched).
+__device__ __forceinline__ uint32_t next_lane_word(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(next_lane_in_tile(__lane_id()) * 4, (int)v);
+}
+
 // A lane's share of one tile row of a 128-column strip. The strip's tile row is
 // 8 tiles of 32*BITS bytes, contiguous; lane = 8t + q holds the BITS dwords at
 // bits 32*BITS*q .. of tile t, which are tile values 32q .. 32q+31 = strip
-// columns 2*lane and 2*lane+1, 16 k values each. w[BITS] is the next lane's
-// first dword (within the tile, q = 7 wrapping to q = 0): it completes the last
-// windows, which reach at most 16 - BITS bits past the lane's own bits.
+// columns 2*lane and 2*lane+1, 16 k values each. The last windows reach at most
+// 16 - BITS bits past the lane's own bits, into the next lane's first dword
+// (within the tile, q = 7 wrapping to q = 0), which comes across with one
+// ds_bpermute: a second load of it would double the wave's memory instructions.
+// Every lane of the wave must be active.
 // Output: wp[c][p] = packed (W[2p][2*lane+c], W[2p+1][2*lane+c]) of the tile row.
 template <int BITS>
-__device__ __forceinline__ void decode_lane(const uint32_t (&w)[BITS + 1], half2_t (&wp)[2][8]) {
+__device__ __forceinline__ void decode_lane(const uint32_t (&w)[BITS], half2_t (&wp)[2][8]) {
+  uint32_t we[BITS + 1];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) we[i] = w[i];
+  we[BITS] = next_lane_word(w[0]);
   uint32_t st[32];
-  lane_states<BITS>(w, st);
+  lane_states<BITS>(we, st);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -175,9 +191,6 @@ __device__ __forceinline__ void decode_column(const uint32_t (&u)[column_words<B
 #pragma unroll
   for (int p = 0; p < 8; ++p) wp[p] = decode_pair(st[2 * p], st[2 * p + 1]);
 }
-
-// Lane that holds the dword following this lane's share inside the same tile.
-__device__ __forceinline__ int next_lane_in_tile(int lane) { return (lane & ~7) | ((lane + 1) & 7); }
 
 // ---------------------------------------------------------------------------
 // 128-point butterflies on one wave: element e of the block lives in lane e % 64,

@@ -60,7 +60,6 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
   const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
   const size_t step_words = (size_t)WAVES * st.row;
   const int off = lane * BITS;
-  const int nb = next_lane_in_tile(lane) * BITS;
 
   // Row r of this pass reads z as dword pairs; padded rows (r >= nr) repeat the
   // last real row and are never stored.
@@ -76,7 +75,7 @@ __global__ __launch_bounds__(kWave* WAVES) void linear_kernel(const uint16_t* __
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r][0] = acc[r][1] = 0.0f;
 
-  StreamWalk<BITS, WAVES, NR> walk{tp, step_words, off, nb, iters};
+  StreamWalk<BITS, WAVES, NR> walk{tp, step_words, off, iters};
   walk.prime();
   walk.run(zrow, acc);
 
@@ -95,11 +94,11 @@ struct LdsWalk {
   static constexpr int RING = PF + 1;
   const uint32_t* __restrict__ tp;
   size_t step_words;
-  int off, nb, iters;
+  int off, iters;
   const uint4* __restrict__ zsrc;  // this lane's 16 bytes of z for step 0
   uint4* zslot;                    // the wave's LDS slot: row r, k-half h at [2r + h]
   bool stager;                     // lane < 2 * NR
-  uint32_t ring[RING][BITS + 1];
+  uint32_t ring[RING][BITS];
   uint4 zn;
 
   __device__ __forceinline__ const uint32_t* share(int i) const {
@@ -110,7 +109,7 @@ struct LdsWalk {
   __device__ __forceinline__ void prime() {
     zn = zload(0);
 #pragma unroll
-    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
+    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off);
   }
 
   // Step i, decoding ring slot D = i % RING; the load for step i + PF refills
@@ -119,7 +118,7 @@ struct LdsWalk {
   __device__ __forceinline__ void step(int i, float (&acc)[NR][2]) {
     const uint4 zc = zn;
     zn = zload(i + 1);  // issued before the next stream load: loads complete in order
-    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off, nb);
+    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off);
     if (stager) zslot[__lane_id()] = zc;
     half2_t wp[2][8];
     decode_lane<BITS>(ring[D], wp);
@@ -179,7 +178,6 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
       trellis + (size_t)wave * st.row + (size_t)strip * st.strip,
       (size_t)WAVES * st.row,
       lane * BITS,
-      next_lane_in_tile(lane) * BITS,
       iters,
       reinterpret_cast<const uint4*>(z + (size_t)(r0 + zr) * in_dim + wave * 16 + (lane & 1) * 8),
       zslot[wave],
@@ -337,8 +335,8 @@ __global__ __launch_bounds__(kWave) void decode_tiles_kernel(const uint32_t* __r
   const int kt = blockIdx.y;
   const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
   const uint32_t* tp = trellis + (size_t)kt * row_words + (size_t)strip * 64 * BITS;
-  uint32_t w[BITS + 1];
-  load_share<BITS>(w, tp, lane * BITS, next_lane_in_tile(lane) * BITS);
+  uint32_t w[BITS];
+  load_share<BITS>(w, tp, lane * BITS);
   half2_t wp[2][8];
   decode_lane<BITS>(w, wp);
 #pragma unroll

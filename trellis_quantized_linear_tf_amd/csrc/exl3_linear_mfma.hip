@@ -71,7 +71,6 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(5)
   const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
   const size_t step_words = (size_t)WAVES * st.row;
   const int off = lane * BITS;
-  const int nb = next_lane_in_tile(lane) * BITS;
   auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
 
   // z staging: lane l < 8 loads row min(l / 2, nr - 1), k-half l % 2.
@@ -91,16 +90,16 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(5)
 #pragma unroll
   for (int c = 0; c < 2; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint32_t ring[RING][BITS + 1];
+  uint32_t ring[RING][BITS];
   uint4 zn = zload(0);
 #pragma unroll
-  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
+  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off);
 
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     const uint4 zc = zn;
     zn = zload(i + 1);  // issued before the next stream load: loads complete in order
-    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off, nb);
+    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off);
     if (stager) zslot[wave][lane] = zc;
     half2_t wp[2][8];
     decode_lane<BITS>(ring[D], wp);
@@ -163,7 +162,6 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
   const size_t step_words = (size_t)WAVES * st.row;
   const int off = lane * BITS;
-  const int nb = next_lane_in_tile(lane) * BITS;
   auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
 
   // z staging: lane l < 32 loads row min(l / 2, nr - 1), k-half l % 2.
@@ -189,12 +187,12 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
 
-  uint32_t ring[RING][BITS + 1];
+  uint32_t ring[RING][BITS];
   uint4 zr[RING];  // z slice of step i travels in ring slot i % RING
 #pragma unroll
   for (int d = 0; d < PF; ++d) {
     zr[d] = zload(d);
-    load_share<BITS>(ring[d], share(d), off, nb);
+    load_share<BITS>(ring[d], share(d), off);
   }
   if (stager) zslot[wave][0][lane] = zr[0];
   half8_t a[2];
@@ -204,7 +202,7 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     zr[(D + PF) % RING] = zload(i + PF);
-    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off, nb);
+    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off);
     uint4* next = zslot[wave][(i + 1) & 1];
     if (stager) next[lane] = zr[(D + 1) % RING];
     half2_t wp[2][8];

@@ -38,8 +38,7 @@ __global__ __launch_bounds__(kWave* WAVES) void project_kernel(const void* __res
 
   const size_t row_words = (size_t)(out_dim / 16) * 8 * BITS;
   StreamWalk<BITS, WAVES, NR> walk{trellis + (size_t)wave * row_words + (size_t)strip * 64 * BITS,
-                                   (size_t)WAVES * row_words, lane * BITS, next_lane_in_tile(lane) * BITS,
-                                   iters};
+                                   (size_t)WAVES * row_words, lane * BITS, iters};
 
   // rot_in of this pass's rows into LDS: wave w takes 128-blocks w, w + WAVES, ...
   // in chunks of kChunk. A chunk's loads all go out before its first use, and the

@@ -38,24 +38,21 @@ constexpr int prefetch_depth() {
   return BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 4 ? 4 : BITS == 8 ? 2 : 3;
 }
 
-// A lane's share of a tile row plus the first dword of the next lane's share,
-// which completes the last windows (it lies in cache lines the wave loads
-// anyway). The stream is read once, so the loads are nontemporal. `p` is the
-// wave-uniform start of the strip's tile row (an SGPR pair), `off` the lane's
-// dword offset and `nb` the next lane's (wrapping inside the tile), so the
-// loads take the scalar-base + vector-offset form.
+// A lane's share of a tile row: BITS dwords (decode_lane fetches the next
+// lane's first dword from that lane). The stream is read once, so the loads are
+// nontemporal. `p` is the wave-uniform start of the strip's tile row (an SGPR
+// pair) and `off` the lane's dword offset, so the loads take the scalar-base +
+// vector-offset form.
 template <int BITS>
-__device__ __forceinline__ void load_share(uint32_t (&dst)[BITS + 1], const uint32_t* __restrict__ p, int off,
-                                           int nb) {
+__device__ __forceinline__ void load_share(uint32_t (&dst)[BITS], const uint32_t* __restrict__ p, int off) {
 #pragma unroll
   for (int i = 0; i < BITS; ++i) dst[i] = __builtin_nontemporal_load(p + off + i);
-  dst[BITS] = __builtin_nontemporal_load(p + nb);
 }
 
 // One tile row of the strip for one wave: decode 32 weights per lane and chain
 // the dot products of every row.
 template <int BITS, int WAVES, int NR>
-__device__ __forceinline__ void tile_row_step(const uint32_t (&w)[BITS + 1], int i,
+__device__ __forceinline__ void tile_row_step(const uint32_t (&w)[BITS], int i,
                                               const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
   half2_t wp[2][8];
   decode_lane<BITS>(w, wp);
@@ -85,8 +82,8 @@ struct StreamWalk {
   static constexpr int RING = PF + 1;
   const uint32_t* __restrict__ tp;
   size_t step_words;
-  int off, nb, iters;
-  uint32_t ring[RING][BITS + 1];
+  int off, iters;
+  uint32_t ring[RING][BITS];
 
   __device__ __forceinline__ const uint32_t* share(int i) const {
     return tp + (size_t)min(i, iters - 1) * step_words;
@@ -94,7 +91,7 @@ struct StreamWalk {
 
   __device__ __forceinline__ void prime() {
 #pragma unroll
-    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off, nb);
+    for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off);
   }
 
   __device__ __forceinline__ void run(const uint32_t* const (&zrow)[NR], float (&acc)[NR][2]) {
@@ -102,7 +99,7 @@ struct StreamWalk {
     for (; it + RING <= iters; it += RING) {
 #pragma unroll
       for (int d = 0; d < RING; ++d) {
-        load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off, nb);
+        load_share<BITS>(ring[(d + PF) % RING], share(it + d + PF), off);
         tile_row_step<BITS, WAVES, NR>(ring[d], it + d, zrow, acc);
       }
     }
