@@ -77,44 +77,75 @@ __global__ __launch_bounds__(kWave * 2 * WAVES) void linear_cs_kernel(const uint
 #pragma unroll
     for (int i = 0; i < ND; ++i) dst[i] = __builtin_nontemporal_load(p + offw[i]);
   };
-  uint4 zn = zload(0);
-#pragma unroll
-  for (int d = 0; d < PF; ++d) load(ring[d], share(d));
-
-  auto step = [&](auto dc, int i) __attribute__((always_inline)) {
-    constexpr int D = decltype(dc)::value;
-    const uint4 zc = zn;
-    zn = zload(i + 1);  // issued before the next stream load: loads complete in order
-    load(ring[(D + PF) % RING], share(i + PF));
-    if (stager) slot[lane] = zc;
+  // The column's 16 weights of ring slot D as (k, k+1) pairs.
+  auto decode = [&](const uint32_t(&w)[ND], half2_t(&wp)[8]) __attribute__((always_inline)) {
     uint32_t u[CW];
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       if constexpr (BITS % 2) {
-        u[j] = __builtin_amdgcn_alignbit(ring[D][j + 1], ring[D][j], shl);
+        u[j] = __builtin_amdgcn_alignbit(w[j + 1], w[j], shl);
       } else {
-        u[j] = ring[D][j];
+        u[j] = w[j];
       }
     }
-    half2_t wp[8];
     decode_column<BITS>(u, wp);
-    // Row r + 1's z is read while row r's chain runs (see linear_lds_kernel).
-    uint4 lo = slot[0];
-    uint4 hi = slot[1];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t zp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (r + 1 < NR) {
-        lo = slot[2 * r + 2];
-        hi = slot[2 * r + 3];
-      }
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-        acc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, zp[p]), wp[p], acc[r], false);
-      asm volatile("" : "+v"(acc[r])::"memory");
-    }
   };
-  step_loop<RING>(iters, step);
+
+  if constexpr (NR <= kScalarZRows) {
+    // Up to 4 rows: the step's z pairs are wave-uniform scalar loads, the SGPR
+    // operand of v_dot2c (as in linear_kernel); no LDS slot, no branch, so one
+    // step's chain can overlap the next step's decode.
+    const uint32_t* zrow[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      zrow[r] = reinterpret_cast<const uint32_t*>(z + (size_t)(r0 + min(r, nr - 1)) * in_dim) + wave * 8;
+#pragma unroll
+    for (int d = 0; d < PF; ++d) load(ring[d], share(d));
+    auto step = [&](auto dc, int i) __attribute__((always_inline)) {
+      constexpr int D = decltype(dc)::value;
+      load(ring[(D + PF) % RING], share(i + PF));
+      half2_t wp[8];
+      decode(ring[D], wp);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t* zp = zrow[r] + (size_t)i * (WAVES * 8);
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          acc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, zp[p]), wp[p], acc[r], false);
+      }
+    };
+    step_loop<RING>(iters, step);
+  } else {
+    uint4 zn = zload(0);
+#pragma unroll
+    for (int d = 0; d < PF; ++d) load(ring[d], share(d));
+
+    auto step = [&](auto dc, int i) __attribute__((always_inline)) {
+      constexpr int D = decltype(dc)::value;
+      const uint4 zc = zn;
+      zn = zload(i + 1);  // issued before the next stream load: loads complete in order
+      load(ring[(D + PF) % RING], share(i + PF));
+      if (stager) slot[lane] = zc;
+      half2_t wp[8];
+      decode(ring[D], wp);
+      // Row r + 1's z is read while row r's chain runs (see linear_lds_kernel).
+      uint4 lo = slot[0];
+      uint4 hi = slot[1];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t zp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if (r + 1 < NR) {
+          lo = slot[2 * r + 2];
+          hi = slot[2 * r + 3];
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          acc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, zp[p]), wp[p], acc[r], false);
+        asm volatile("" : "+v"(acc[r])::"memory");
+      }
+    };
+    step_loop<RING>(iters, step);
+  }
 
   // Wave (h, w)'s sums go to partial[w][row][64h + lane]; the finish adds the
   // WAVES tile-row waves in order, FR rows per round.
