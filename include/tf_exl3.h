@@ -154,9 +154,9 @@ int tf_exl3_linear_prompt(int bits, int rows, int in_dim, int out_dim, const uin
 /*
  * linear_mfma: the same projection with the same arguments, refusals, stream
  * format and finish, but the sums over k run on the matrix cores
- * (v_mfma_f32_16x16x32_f16 for passes of up to 4 rows, v_mfma_f32_32x32x16_f16
- * for 5 to 16; the two give the same bits) instead of v_dot2 chains, so the
- * vector ALUs only decode and the time grows slowly with the rows. Its k order per
+ * (v_mfma_f32_16x16x32_f16 over pairs of tile rows, one instruction shape for
+ * every pass of 1 to 16 rows) instead of v_dot2 chains, so the vector ALUs only
+ * decode and the time grows slowly with the rows. Its k order per
  * output is fixed by (in_dim, waves) and never depends on the rows sharing the
  * launch; it is a different fixed order from tf_exl3_linear's, so the two agree
  * to the float64 gate, not bit for bit. (The page's "Known limits" and the

@@ -1,38 +1,32 @@
 // The trellis linear with the row-by-weight products on the matrix cores.
 //
-// Same projection, stream walk, decode and finish as the v_dot2 linear (TensorFold
-// pull request "hip exl3: the input rotation and trellis linear for decode
-// rows", "What this changes"); only the sums over k move from v_dot2_f32_f16
-// chains to the matrix cores, so the vector ALUs spend their cycles on decoding
-// and the cost grows slowly with the number of rows.
+// Same projection, stream format, decode and finish as the v_dot2 linear
+// (TensorFold pull request "hip exl3: the input rotation and trellis linear for
+// decode rows", "What this changes"); only the sums over k move from
+// v_dot2_f32_f16 chains to v_mfma_f32_16x16x32_f16, so the vector ALUs spend
+// their cycles on decoding and the time grows slowly with the number of rows.
 //
-// Lane l decodes strip columns 2l and 2l+1 for the 16 k of a tile row kt, as
-// packed (k, k+1) pairs wp[c][0..7] (column parity c). For each k-half q the
-// four pairs wp[c][4q .. 4q+3] (8 k of one column) are the lane's B operand,
-// unchanged. B's k-groups therefore mix strip columns; the A operand undoes the
-// mix by carrying a row's inputs only in the k-group of the columns it sums:
-//
-// Passes of up to 4 rows, v_mfma_f32_16x16x32_f16 (lane l = 16G + n):
-//  - B (32 k x 16 n): B[8G + t][n] = W[16kt + 8q + t][2l + c]: column 32G + 2n + c;
-//  - A (16 m x 32 k): row m = 4r + g holds pass row r's z[16kt + 8q + t] in
-//    k-group g only, so D[4r + g][n] sums strip column 32g + 2n + c of row r;
-//    lane 16G + m holds A[m][8G .. 8G+7], non-zero iff m % 4 == G;
-//  - D: lane l holds D[4G + i][n], i = 0..3: row G, strip column 32i + 2n + c.
-// Passes of 5 to 16 rows, v_mfma_f32_32x32x16_f16 (lane l = 32h + j):
-//  - B (16 k x 32 n): B[8h + t][j] = W[16kt + 8q + t][2l + c]: column 64h + 2j + c;
-//  - A (32 m x 16 k): row m = 2r + g holds row r's z in k-half g only; lane
-//    32h + i holds A[i][8h .. 8h+7], non-zero iff i % 2 == h;
-//  - D: lane l holds rows m = 8(v/4) + 4h + v%4, v = 0..15 (row m/2, strip
-//    column 64(m%2) + 2j + c).
-// The row inputs of a step (rows x 16 k) come in with one 16-byte vector load
-// per lane, one step ahead and ahead of the stream load (loads complete in
-// order), into a wave-private LDS slot; each lane reads its A operand from there,
-// and lanes whose A is zero read a zero entry. Every output sums the same eight
-// non-zero products per instruction, in the same k order (tile rows in the
-// wave's order, q = 0 then 1), and a row's D entries depend only on its own A
-// row; the two instruction shapes give the same bits (tested with rows alone,
-// in windows and in multi-pass launches), so a row's bits never depend on the
-// rows that share the launch.
+// One workgroup per (128-column strip, pass of up to 16 rows). A wave step
+// covers a pair of tile rows, k = 32p .. 32p + 31 (wave w takes p = w, w +
+// WAVES, ...), and runs eight MFMAs, one per 16-column tile m of the strip:
+//  - B (32 k x 16 n): lane l = 16g + n holds B[8g + t][n] = W[32p + 8g + t]
+//    [128 strip + 16m + n], t = 0..7: k-group g is tile row 2p + (g >> 1),
+//    k-half g & 1, of column n of tile m. These 8 values are 8 consecutive
+//    windows of the tile (value index 16n + 8(g & 1) + t), so the lane loads
+//    the 2 or 3 dwords that hold their 7*BITS + 16 bits (wrapping inside the
+//    tile), realigns them when the k-half does not start on a dword, and
+//    decodes its B operand directly: no lane exchange, no zero padding;
+//  - A (16 rows x 32 k): lane 16g + r holds z[r][32p + 8g .. 32p + 8g + 7],
+//    one 16-byte load per lane per step (rows past the pass repeat its last
+//    row and are never stored);
+//  - D: lane 16g + n holds D[4g + i][n], i = 0..3: pass row 4g + i, strip
+//    column 16m + n.
+// A row's D entries depend only on its own A row, and every pass, whatever its
+// row count, runs the same instruction over the same k groups in the same
+// order (pairs ascending per wave, then the waves' sums in wave order), so a
+// row's bits never depend on the rows that share its launch. The order is a
+// different fixed one from the v_dot2 linear's: the two agree to the float64
+// gate, not bit for bit.
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
@@ -50,233 +44,186 @@ __device__ __forceinline__ half8_t pairs_to_half8(half2_t a, half2_t b, half2_t 
   return __builtin_bit_cast(half8_t, u);
 }
 
-// Passes of up to 4 rows on v_mfma_f32_16x16x32_f16.
-template <int BITS, int WAVES>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(5))) void linear_mfma_kernel(
-    const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
-    void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
-  constexpr int NR = 4;
-  constexpr int PF = prefetch_depth<BITS>();
-  constexpr int RING = PF + 1;
-  __shared__ float partial[WAVES * NR * kBlock];
-  __shared__ uint4 zslot[WAVES][2 * NR + 1];  // row r, k-half h at [2r + h]; [2 * NR] stays zero
-
-  const int lane = __lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int strip = blockIdx.x;
-  const int nr = min(NR, rows);
-  const int iters = in_dim / 16 / WAVES;
-
-  const StreamStrides st = stream_strides<BITS>(kLayoutTiles, in_dim, out_dim);
-  const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
-  const size_t step_words = (size_t)WAVES * st.row;
-  const int off = lane * BITS;
-  auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
-
-  // z staging: lane l < 8 loads row min(l / 2, nr - 1), k-half l % 2.
-  const bool stager = lane < 2 * NR;
-  const uint4* __restrict__ zsrc = reinterpret_cast<const uint4*>(
-      z + (size_t)min(lane >> 1, nr - 1) * in_dim + wave * 16 + (lane & 1) * 8);
-  auto zload = [&](int i) { return zsrc[(size_t)min(i, iters - 1) * (WAVES * 2)]; };
-  if (lane == 0) zslot[wave][2 * NR] = make_uint4(0u, 0u, 0u, 0u);
-
-  // A address: lane 16G + m reads row min(m / 4, nr - 1) iff m % 4 == G.
-  const int m = lane & 15;
-  const bool part = (m & 3) == (lane >> 4);
-  const int abase = part ? 2 * min(m >> 2, nr - 1) : 2 * NR;
-  const int aq = part ? 1 : 0;
-
-  f32x4 acc[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  uint32_t ring[RING][BITS];
-  uint4 zn = zload(0);
-#pragma unroll
-  for (int d = 0; d < PF; ++d) load_share<BITS>(ring[d], share(d), off);
-
-  auto step = [&](auto dc, int i) __attribute__((always_inline)) {
-    constexpr int D = decltype(dc)::value;
-    const uint4 zc = zn;
-    zn = zload(i + 1);  // issued before the next stream load: loads complete in order
-    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off);
-    if (stager) zslot[wave][lane] = zc;
-    half2_t wp[2][8];
-    decode_lane<BITS>(ring[D], wp);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const half8_t a = __builtin_bit_cast(half8_t, zslot[wave][abase + q * aq]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const half8_t b = pairs_to_half8(wp[c][4 * q], wp[c][4 * q + 1], wp[c][4 * q + 2], wp[c][4 * q + 3]);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
-      }
-    }
-  };
-  step_loop<RING>(iters, step);
-
-  // D entry i of acc[c]: pass row G, strip column 32i + 2n + c.
-  const int n = lane & 15;
-  const int r = lane >> 4;
-  if (r < nr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float2 v;
-      v.x = acc[0][i];
-      v.y = acc[1][i];
-      *reinterpret_cast<float2*>(&partial[(wave * NR + r) * kBlock + 32 * i + 2 * n]) = v;
-    }
-  }
-  __syncthreads();
-  finish_strip<WAVES>(partial, NR, wave, lane, nr, 0, strip, out_dim, svh, y, y_dtype);
+// Dwords a lane loads for one k-half: its windows span 7*BITS + 16 bits and
+// start at bit (16n + 8h)*BITS of the tile, up to 24 bits into a dword.
+template <int BITS>
+constexpr int khalf_raw_words() {
+  return BITS <= 4 ? 2 : 3;
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Realigned dwords (bit 0 = the first window's bit 0) that hold the 8 windows.
+template <int BITS>
+constexpr int khalf_words() {
+  return (7 * BITS + 16 + 31) / 32;
+}
 
-// Passes of up to 16 rows on v_mfma_f32_32x32x16_f16. Pipeline per step i: the
-// loads for step i + PF (z slice, then stream share: z never waits behind a
-// younger stream load), the z slice of step i + 1 into LDS slot (i + 1) % 2,
-// the decode of step i, its MFMAs with the A operands read at the end of step
-// i - 1, then the A operands of step i + 1 (their latency hides behind the next
-// step's loads and decode).
+// Whether every k-half starts on a dword boundary (4 and 8 bits), so no
+// realignment is needed.
+template <int BITS>
+constexpr bool khalf_aligned() {
+  return (8 * BITS) % 32 == 0;
+}
+
+// The 8 states of a k-half from its realigned dwords a[] (window j at bit
+// j*BITS; a[khalf_words] is zero). When BITS divides 16 and the window 16 bits
+// on is in the same k-half, one funnel shift gives both (as in lane_states).
+template <int BITS, int I = 0>
+__device__ __forceinline__ void khalf_states(const uint32_t (&a)[khalf_words<BITS>() + 1], uint32_t (&st)[8]) {
+  if constexpr (I < 8) {
+    constexpr int o = I * BITS;
+    constexpr int d = o >> 5;
+    constexpr int sh = o & 31;
+    if constexpr (16 % BITS == 0 && 16 / BITS < 8) {
+      if constexpr (sh < 16) {
+        uint32_t t;
+        if constexpr (sh == 0) {
+          t = a[d];
+        } else {
+          t = funnel<sh>(a[d + 1], a[d]);
+        }
+        st[I] = t & 0xFFFFu;
+        if constexpr (I + 16 / BITS < 8) st[I + 16 / BITS] = t >> 16;
+      }
+    } else {
+      st[I] = window_at<BITS>(a, I);
+    }
+    khalf_states<BITS, I + 1>(a, st);
+  }
+}
+
+// Per-wave LDS: while the wave walks, the stage of one pair's stream (two tile
+// rows, the second kStagePad words further so the two halves of the wave read
+// different banks); afterwards the wave's partial sums [16 rows][128] fp32.
+constexpr int kStagePad = 32;
+template <int BITS>
+constexpr int stage_words() {
+  return 2 * 64 * BITS + kStagePad;
+}
+constexpr int kWaveLdsWords = kRowsPerPass * kBlock;  // 8 KiB per wave
+
 template <int BITS, int WAVES>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma32_kernel(
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
   constexpr int NR = kRowsPerPass;
-  constexpr int PF = prefetch_depth<BITS>() < 4 ? prefetch_depth<BITS>() : 4;  // z rides in the ring too
+  constexpr int CW = khalf_raw_words<BITS>();
+  constexpr int KW = khalf_words<BITS>();
+  constexpr int PF = prefetch_depth<BITS>() / 2 > 0 ? prefetch_depth<BITS>() / 2 : 1;  // pairs in flight
   constexpr int RING = PF + 1;
-  constexpr int FR = 8;  // rows per finish round: 32 KiB of partial sums at 8 waves
-  constexpr int SLOT = 2 * NR + 1;  // row r, k-half h at [2r + h]; [2 * NR] stays zero
-  __shared__ float partial[WAVES * FR * kBlock];
-  __shared__ uint4 zslot[WAVES][2][SLOT];
+  constexpr int ROW_STRIDE = 64 * BITS + kStagePad;  // stage words from tile row 2p to 2p + 1
+  static_assert(stage_words<BITS>() <= kWaveLdsWords, "the stage fits the wave's partial-sum area");
+  __shared__ __attribute__((aligned(16))) uint32_t lds[WAVES * kWaveLdsWords];
 
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int strip = blockIdx.x;
   const int r0 = blockIdx.y * NR;
   const int nr = min(NR, rows - r0);
-  const int iters = in_dim / 16 / WAVES;
+  const int pairs = in_dim / 32;
+  const int iters = (pairs - wave + WAVES - 1) / WAVES;  // 0 when in_dim = 128 and WAVES = 8, wave >= 4
+  uint32_t* const stage = lds + wave * kWaveLdsWords;
 
+  // Stream walk: the strip's tile rows 2p and 2p + 1 of the wave's pair p, each
+  // one coalesced load of 64*BITS dwords (BITS per lane, as in the v_dot2 linear).
   const StreamStrides st = stream_strides<BITS>(kLayoutTiles, in_dim, out_dim);
-  const uint32_t* __restrict__ tp = trellis + (size_t)wave * st.row + (size_t)strip * st.strip;
-  const size_t step_words = (size_t)WAVES * st.row;
+  const uint32_t* __restrict__ tbase = trellis + (size_t)strip * st.strip;
   const int off = lane * BITS;
-  auto share = [&](int i) { return tp + (size_t)min(i, iters - 1) * step_words; };
+  auto pair_ptr = [&](int i) { return tbase + (size_t)(2 * min(wave + i * WAVES, pairs - 1)) * st.row; };
+  // A operand: lane 16g + r holds z[r][32p + 8g .. + 7] (rows past the pass repeat its last row).
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const uint4* __restrict__ zsrc =
+      reinterpret_cast<const uint4*>(z + (size_t)(r0 + min(n, nr - 1)) * in_dim + 8 * g);
+  auto zload = [&](int i) { return zsrc[(size_t)min(wave + i * WAVES, pairs - 1) * 4]; };
 
-  // z staging: lane l < 32 loads row min(l / 2, nr - 1), k-half l % 2.
-  const bool stager = lane < 2 * NR;
-  const uint4* __restrict__ zsrc = reinterpret_cast<const uint4*>(
-      z + (size_t)(r0 + min(lane >> 1, nr - 1)) * in_dim + wave * 16 + (lane & 1) * 8);
-  auto zload = [&](int i) { return zsrc[(size_t)min(i, iters - 1) * (WAVES * 2)]; };
-  if (lane == 0) {
-    zslot[wave][0][2 * NR] = make_uint4(0u, 0u, 0u, 0u);
-    zslot[wave][1][2 * NR] = make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  // A address: lane 32h + i reads row min(i / 2, nr - 1) iff i % 2 == h.
-  const int ai = lane & 31;
-  const int ah = lane >> 5;
-  const bool part = (ai & 1) == ah;
-  const int abase = part ? 2 * min(ai >> 1, nr - 1) : 2 * NR;
-  const int aq = part ? 1 : 0;
-
-  f32x16 acc[2];
+  // B operand: lane 16g + n decodes k-half g & 1 of column n of every tile of tile
+  // row 2p + (g >> 1); its dwords sit at these stage offsets (tile m adds 8*BITS*m).
+  const int bit0 = (16 * n + 8 * (g & 1)) * BITS;
+  const int sh = bit0 & 31;
+  int roff[CW];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  for (int c = 0; c < CW; ++c) roff[c] = (g >> 1) * ROW_STRIDE + ((bit0 >> 5) + c) % (8 * BITS);
 
-  uint32_t ring[RING][BITS];
-  uint4 zr[RING];  // z slice of step i travels in ring slot i % RING
+  uint32_t ring[RING][2][BITS];
+  uint4 zr[RING];
+  auto issue = [&](uint32_t (&dst)[2][BITS], uint4& zd, int i) __attribute__((always_inline)) {
+    zd = zload(i);
+    const uint32_t* p = pair_ptr(i);
+    load_share<BITS>(dst[0], p, off);
+    load_share<BITS>(dst[1], p + st.row, off);
+  };
+  auto put = [&](const uint32_t (&src)[2][BITS]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int d = 0; d < PF; ++d) {
-    zr[d] = zload(d);
-    load_share<BITS>(ring[d], share(d), off);
-  }
-  if (stager) zslot[wave][0][lane] = zr[0];
-  half8_t a[2];
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) a[q] = __builtin_bit_cast(half8_t, zslot[wave][0][abase + q * aq]);
+      for (int c = 0; c < BITS; ++c) stage[t * ROW_STRIDE + off + c] = src[t][c];
+    }
+  };
 
+  f32x4 acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int d = 0; d < PF; ++d) issue(ring[d], zr[d], d);
+  put(ring[0]);
+
+  // Step i: loads for step i + PF; this step's dwords out of the stage; step
+  // i + 1's stream into the stage (LDS runs a wave's accesses in order, so the
+  // reads above see step i); decode and eight MFMAs.
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
-    zr[(D + PF) % RING] = zload(i + PF);
-    load_share<BITS>(ring[(D + PF) % RING], share(i + PF), off);
-    uint4* next = zslot[wave][(i + 1) & 1];
-    if (stager) next[lane] = zr[(D + 1) % RING];
-    half2_t wp[2][8];
-    decode_lane<BITS>(ring[D], wp);
+    issue(ring[(D + PF) % RING], zr[(D + PF) % RING], i + PF);
+    uint32_t kh[8][CW];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int m = 0; m < 8; ++m) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const half8_t b = pairs_to_half8(wp[c][4 * q], wp[c][4 * q + 1], wp[c][4 * q + 2], wp[c][4 * q + 3]);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[q], b, acc[c], 0, 0, 0);
-      }
+      for (int c = 0; c < CW; ++c) kh[m][c] = stage[roff[c] + m * 8 * BITS];
     }
+    put(ring[(D + 1) % RING]);
+    const half8_t a = __builtin_bit_cast(half8_t, zr[D]);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) a[q] = __builtin_bit_cast(half8_t, next[abase + q * aq]);
+    for (int m = 0; m < 8; ++m) {
+      uint32_t al[KW + 1];
+#pragma unroll
+      for (int c = 0; c < KW; ++c) {
+        if constexpr (khalf_aligned<BITS>()) {
+          al[c] = kh[m][c];
+        } else {
+          al[c] = __builtin_amdgcn_alignbit(c + 1 < CW ? kh[m][c + 1] : 0u, kh[m][c], sh);
+        }
+      }
+      al[KW] = 0u;
+      uint32_t s8[8];
+      khalf_states<BITS>(al, s8);
+      const half8_t b = pairs_to_half8(decode_pair(s8[0], s8[1]), decode_pair(s8[2], s8[3]),
+                                       decode_pair(s8[4], s8[5]), decode_pair(s8[6], s8[7]));
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[m], 0, 0, 0);
+    }
   };
   step_loop<RING>(iters, step);
 
-  // D entry v of acc[c]: row m = 8(v/4) + 4h + v%4 (pass row m/2, k-half g = m%2),
-  // strip column 64g + 2j + c. Rows 8 at a time: v/4 = 2 * round + {0, 1}.
-  const int j = lane & 31;
+  // D entry i of acc[m]: pass row 4g + i, strip column 16m + n. The wave's stage
+  // becomes its partial sums (its own reads are done: LDS keeps the wave's order).
+  float* const partial = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int round = 0; round < NR / FR; ++round) {
-    if (round * FR >= nr) break;  // block-uniform
-    if (round > 0) __syncthreads();  // the previous round has read partial
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    if (r < nr) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int v = 8 * round; v < 8 * round + 8; ++v) {
-        const int m = 8 * (v >> 2) + 4 * ah + (v & 3);
-        const int r = m >> 1;
-        if (r < nr) partial[(wave * FR + r - FR * round) * kBlock + 64 * (m & 1) + 2 * j + c] = acc[c][v];
-      }
+      for (int m = 0; m < 8; ++m) partial[(wave * NR + r) * kBlock + 16 * m + n] = acc[m][i];
     }
-    __syncthreads();
-    finish_strip<WAVES>(partial, FR, wave, lane, min(FR, nr - FR * round), r0 + FR * round, strip, out_dim, svh,
-                        y, y_dtype);
   }
-}
-
-template <int BITS, int WAVES>
-static void launch_4(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
-                     const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES>), dim3(out_dim / kBlock), dim3(kWave * WAVES), 0, stream, z,
-                     trellis, svh, y, y_dtype, rows, in_dim, out_dim);
-}
-
-template <int BITS, int WAVES>
-static void launch_32(dim3 grid, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
-                      const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_mfma32_kernel<BITS, WAVES>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh, y,
-                     y_dtype, rows, in_dim, out_dim);
+  __syncthreads();
+  finish_strip<WAVES>(partial, NR, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
 template <int BITS, int WAVES>
 static hipError_t launch_mfma_bw(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
                                  const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
-  const int full = rows / kRowsPerPass;
-  const int rest = rows % kRowsPerPass;
-  const int strips = out_dim / kBlock;
-  if (full > 0)
-    launch_32<BITS, WAVES>(dim3(strips, full), full * kRowsPerPass, in_dim, out_dim, z, trellis, svh, y, y_dtype,
-                           stream);
-  if (rest > 0) {
-    const size_t off = (size_t)full * kRowsPerPass;
-    const uint16_t* zr = z + off * in_dim;
-    void* yr = (y_dtype == TF_DT_F32) ? (void*)(static_cast<float*>(y) + off * out_dim)
-                                      : (void*)(static_cast<uint16_t*>(y) + off * out_dim);
-    const dim3 grid(strips, 1);
-    if (rest <= 4) {
-      launch_4<BITS, WAVES>(rest, in_dim, out_dim, zr, trellis, svh, yr, y_dtype, stream);
-    } else {
-      launch_32<BITS, WAVES>(grid, rest, in_dim, out_dim, zr, trellis, svh, yr, y_dtype, stream);
-    }
-  }
+  const dim3 grid(out_dim / kBlock, (rows + kRowsPerPass - 1) / kRowsPerPass);
+  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh, y,
+                     y_dtype, rows, in_dim, out_dim);
   return hipGetLastError();
 }
 
