@@ -35,7 +35,8 @@ def make(bits, k, n, rows, seed, sigma=1.0):
 @ENGINES
 @pytest.mark.parametrize("bits", tr.WIDTHS)
 @pytest.mark.parametrize("waves", [4, 8])
-@pytest.mark.parametrize("k,n,rows", [(128, 128, 1), (256, 384, 3), (512, 1024, 17), (1024, 256, 33)])
+@pytest.mark.parametrize("k,n,rows", [(128, 128, 1), (256, 384, 3), (384, 256, 5), (640, 128, 2), (512, 1024, 17),
+                                       (1024, 256, 33)])
 def test_small_shapes_gate(gpu, engine, bits, waves, k, n, rows):
     stream, z, svh = make(bits, k, n, rows, 1000 * bits + k + rows)
     say(f"linear {engine} bits={bits} waves={waves} k={k} n={n} rows={rows}")
