@@ -156,7 +156,9 @@ int tf_exl3_linear_prompt(int bits, int rows, int in_dim, int out_dim, const uin
  * format and finish, but the sums over k run on the matrix cores
  * (v_mfma_f32_16x16x32_f16 over pairs of tile rows, one instruction shape for
  * every pass of 1 to 16 rows) instead of v_dot2 chains, so the vector ALUs only
- * decode and the time grows slowly with the rows. Its k order per
+ * decode and the time grows slowly with the rows. At 4 waves, a matrix with
+ * fewer than 256 strips runs a column-split form (twice the waves per strip, the
+ * same MFMAs per column, the same bits). Its k order per
  * output is fixed by (in_dim, waves) and never depends on the rows sharing the
  * launch; it is a different fixed order from tf_exl3_linear's, so the two agree
  * to the float64 gate, not bit for bit. (The page's "Known limits" and the

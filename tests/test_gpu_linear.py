@@ -180,3 +180,23 @@ def test_engines_agree(gpu, bits):
     b = linear(z, stream, svh, bits, n, engine="mfma")
     y64 = lin.linear_f64(z, stream, bits, k, n, svh)
     assert lin.gate_error(a, "f32", y64) <= lin.GATE and lin.gate_error(b, "f32", y64) <= lin.GATE
+
+
+@pytest.mark.parametrize("bits", tr.WIDTHS)
+@pytest.mark.parametrize("k,rows", [(256, 5), (384, 17)])
+def test_mfma_column_split_same_bits(gpu, bits, k, rows):
+    """At 4 waves the matrix-core linear splits each strip's columns over twice the
+    waves when fewer than 256 strips would leave SIMDs idle; each column keeps its
+    MFMAs and cross-wave order. A narrow matrix made of the first 8 strips of a wide
+    one (which runs the unsplit form) gives the wide run's bits for those columns."""
+    n_wide, n_narrow = 32768, 1024
+    wide = synth.trellis_words(900 + bits + k, bits, k, n_wide)
+    narrow = np.ascontiguousarray(tr.tile_grid(wide, bits, k, n_wide)[:, : n_narrow // 16]).reshape(-1)
+    z = synth.rows(901 + bits, rows, k, "f16")
+    svh = synth.signs(902 + bits, n_wide)
+    say(f"mfma column split bits={bits} k={k} rows={rows}")
+    yw = linear(z, wide, svh, bits, n_wide, "f32", 4, engine="mfma")
+    yn = linear(z, narrow, svh[:n_narrow], bits, n_narrow, "f32", 4, engine="mfma")
+    assert same_bits(yn, yw[:, :n_narrow])
+    y64 = lin.linear_f64(z, narrow, bits, k, n_narrow, svh[:n_narrow])
+    assert lin.gate_error(yn, "f32", y64) <= lin.GATE

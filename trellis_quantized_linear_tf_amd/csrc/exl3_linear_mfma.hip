@@ -91,43 +91,64 @@ __device__ __forceinline__ void khalf_states(const uint32_t (&a)[khalf_words<BIT
   }
 }
 
-// Per-wave LDS: while the wave walks, the stage of one pair's stream (two tile
-// rows, the second kStagePad words further so the two halves of the wave read
-// different banks); afterwards the wave's partial sums [16 rows][128] fp32.
-constexpr int kStagePad = 32;
-template <int BITS>
-constexpr int stage_words() {
-  return 2 * 64 * BITS + kStagePad;
+// LDS stage of one pair's stream for one wave: two tile rows of the wave's
+// tiles (all 8, or 4 in the column-split form), the second padded to start 32
+// banks (mod 64) after the first, so the two halves of the wave, which read
+// different tile rows, read different banks.
+template <int BITS, int HALVES>
+constexpr int stage_row_words() {
+  return 64 * BITS / HALVES + (96 - (64 * BITS / HALVES) % 64) % 64;
 }
-constexpr int kWaveLdsWords = kRowsPerPass * kBlock;  // 8 KiB per wave
+template <int BITS, int HALVES>
+constexpr int stage_words() {
+  return 2 * stage_row_words<BITS, HALVES>();
+}
+constexpr int kWaveLdsWords = kRowsPerPass * kBlock;  // one k-wave's partial sums, 8 KiB
 
-template <int BITS, int WAVES>
-__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
+// HALVES = 1: WAVES waves, each decodes all 8 tiles of its pairs; its stage
+// lives in its own partial-sum area. HALVES = 2 (column split, for launches with
+// fewer waves than SIMDs): 2 * WAVES waves, wave (h, w) takes the same pairs as
+// wave w of the first form but only tiles 4h .. 4h + 3 (strip columns 64h ..
+// 64h + 63), so each column sees the same MFMAs in the same order and the same
+// cross-wave sum: the outputs are bit-identical to the first form's.
+template <int BITS, int WAVES, int HALVES>
+__global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
   constexpr int NR = kRowsPerPass;
+  constexpr int NT = 8 / HALVES;  // tiles (MFMAs) per wave and pair
   constexpr int CW = khalf_raw_words<BITS>();
   constexpr int KW = khalf_words<BITS>();
   constexpr int PF = prefetch_depth<BITS>() / 2 > 0 ? prefetch_depth<BITS>() / 2 : 1;  // pairs in flight
   constexpr int RING = PF + 1;
-  constexpr int ROW_STRIDE = 64 * BITS + kStagePad;  // stage words from tile row 2p to 2p + 1
-  static_assert(stage_words<BITS>() <= kWaveLdsWords, "the stage fits the wave's partial-sum area");
-  __shared__ __attribute__((aligned(16))) uint32_t lds[WAVES * kWaveLdsWords];
+  constexpr int RS = stage_row_words<BITS, HALVES>();  // stage words from tile row 2p to 2p + 1
+  // Loads of a tile row's NT tiles (8 * BITS * NT words): LW lanes take PW contiguous dwords each.
+  constexpr int LW = HALVES == 1 || BITS % 2 == 0 ? kWave : kWave / 2;
+  constexpr int PW = 8 * BITS * NT / LW;
+  static_assert(LW * PW == 8 * BITS * NT, "the wave's loads cover its tiles");
+  static_assert(HALVES == 1 ? stage_words<BITS, 1>() <= kWaveLdsWords : true, "the stage fits the partial area");
+  constexpr int LDS_WORDS = HALVES == 1 ? WAVES * kWaveLdsWords
+                                        : WAVES * kWaveLdsWords + WAVES * HALVES * stage_words<BITS, HALVES>();
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_WORDS];
 
   const int lane = __lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = hw / WAVES;
+  const int wave = hw - half * WAVES;  // the k split, as in the first form
   const int strip = blockIdx.x;
   const int r0 = blockIdx.y * NR;
   const int nr = min(NR, rows - r0);
   const int pairs = in_dim / 32;
   const int iters = (pairs - wave + WAVES - 1) / WAVES;  // 0 when in_dim = 128 and WAVES = 8, wave >= 4
-  uint32_t* const stage = lds + wave * kWaveLdsWords;
+  uint32_t* const stage = HALVES == 1 ? lds + wave * kWaveLdsWords
+                                      : lds + WAVES * kWaveLdsWords + hw * stage_words<BITS, HALVES>();
 
-  // Stream walk: the strip's tile rows 2p and 2p + 1 of the wave's pair p, each
-  // one coalesced load of 64*BITS dwords (BITS per lane, as in the v_dot2 linear).
+  // Stream walk: tile rows 2p and 2p + 1 of the wave's pair p, its NT tiles of
+  // each (one coalesced load per tile row; in the split form at odd widths half
+  // the lanes repeat the other half's words, which they write to the same place).
   const StreamStrides st = stream_strides<BITS>(kLayoutTiles, in_dim, out_dim);
-  const uint32_t* __restrict__ tbase = trellis + (size_t)strip * st.strip;
-  const int off = lane * BITS;
+  const uint32_t* __restrict__ tbase = trellis + (size_t)strip * st.strip + half * NT * 8 * BITS;
+  const int off = (lane % LW) * PW;
   auto pair_ptr = [&](int i) { return tbase + (size_t)(2 * min(wave + i * WAVES, pairs - 1)) * st.row; };
   // A operand: lane 16g + r holds z[r][32p + 8g .. + 7] (rows past the pass repeat its last row).
   const int g = lane >> 4;
@@ -136,33 +157,34 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
       reinterpret_cast<const uint4*>(z + (size_t)(r0 + min(n, nr - 1)) * in_dim + 8 * g);
   auto zload = [&](int i) { return zsrc[(size_t)min(wave + i * WAVES, pairs - 1) * 4]; };
 
-  // B operand: lane 16g + n decodes k-half g & 1 of column n of every tile of tile
-  // row 2p + (g >> 1); its dwords sit at these stage offsets (tile m adds 8*BITS*m).
+  // B operand: lane 16g + n decodes k-half g & 1 of column n of each of the
+  // wave's tiles in tile row 2p + (g >> 1); its dwords sit at these stage
+  // offsets (tile m adds 8*BITS*m).
   const int bit0 = (16 * n + 8 * (g & 1)) * BITS;
   const int sh = bit0 & 31;
   int roff[CW];
 #pragma unroll
-  for (int c = 0; c < CW; ++c) roff[c] = (g >> 1) * ROW_STRIDE + ((bit0 >> 5) + c) % (8 * BITS);
+  for (int c = 0; c < CW; ++c) roff[c] = (g >> 1) * RS + ((bit0 >> 5) + c) % (8 * BITS);
 
-  uint32_t ring[RING][2][BITS];
+  uint32_t ring[RING][2][PW];
   uint4 zr[RING];
-  auto issue = [&](uint32_t (&dst)[2][BITS], uint4& zd, int i) __attribute__((always_inline)) {
+  auto issue = [&](uint32_t (&dst)[2][PW], uint4& zd, int i) __attribute__((always_inline)) {
     zd = zload(i);
     const uint32_t* p = pair_ptr(i);
-    load_share<BITS>(dst[0], p, off);
-    load_share<BITS>(dst[1], p + st.row, off);
+    load_share<PW>(dst[0], p, off);
+    load_share<PW>(dst[1], p + st.row, off);
   };
-  auto put = [&](const uint32_t (&src)[2][BITS]) __attribute__((always_inline)) {
+  auto put = [&](const uint32_t (&src)[2][PW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int c = 0; c < BITS; ++c) stage[t * ROW_STRIDE + off + c] = src[t][c];
+      for (int c = 0; c < PW; ++c) stage[t * RS + off + c] = src[t][c];
     }
   };
 
-  f32x4 acc[8];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
   for (int d = 0; d < PF; ++d) issue(ring[d], zr[d], d);
@@ -170,20 +192,20 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
 
   // Step i: loads for step i + PF; this step's dwords out of the stage; step
   // i + 1's stream into the stage (LDS runs a wave's accesses in order, so the
-  // reads above see step i); decode and eight MFMAs.
+  // reads above see step i); decode and the MFMAs.
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     issue(ring[(D + PF) % RING], zr[(D + PF) % RING], i + PF);
-    uint32_t kh[8][CW];
+    uint32_t kh[NT][CW];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < NT; ++m) {
 #pragma unroll
       for (int c = 0; c < CW; ++c) kh[m][c] = stage[roff[c] + m * 8 * BITS];
     }
     put(ring[(D + 1) % RING]);
     const half8_t a = __builtin_bit_cast(half8_t, zr[D]);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < NT; ++m) {
       uint32_t al[KW + 1];
 #pragma unroll
       for (int c = 0; c < KW; ++c) {
@@ -203,49 +225,55 @@ __global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(4)
   };
   step_loop<RING>(iters, step);
 
-  // D entry i of acc[m]: pass row 4g + i, strip column 16m + n. The wave's stage
-  // becomes its partial sums (its own reads are done: LDS keeps the wave's order).
+  // D entry i of acc[m]: pass row 4g + i, strip column 16 (NT half + m) + n, into
+  // k-wave `wave`'s partial sums (in the first form that area held the wave's
+  // stage, whose reads are done: LDS keeps the wave's order).
   float* const partial = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * g + i;
     if (r < nr) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) partial[(wave * NR + r) * kBlock + 16 * m + n] = acc[m][i];
+      for (int m = 0; m < NT; ++m) partial[(wave * NR + r) * kBlock + 16 * (NT * half + m) + n] = acc[m][i];
     }
   }
   __syncthreads();
-  finish_strip<WAVES>(partial, NR, wave, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
+  finish_strip<WAVES, WAVES * HALVES>(partial, NR, hw, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
-template <int BITS, int WAVES>
-static hipError_t launch_mfma_bw(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
-                                 const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
+template <int BITS, int WAVES, int HALVES>
+static hipError_t launch_mfma_bwh(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
+                                  const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
   const dim3 grid(out_dim / kBlock, (rows + kRowsPerPass - 1) / kRowsPerPass);
-  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES>), grid, dim3(kWave * WAVES), 0, stream, z, trellis, svh, y,
-                     y_dtype, rows, in_dim, out_dim);
+  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES, HALVES>), grid, dim3(kWave * WAVES * HALVES), 0, stream, z,
+                     trellis, svh, y, y_dtype, rows, in_dim, out_dim);
   return hipGetLastError();
 }
 
+// The column-split form runs where the first form would put fewer waves than
+// the device has SIMDs (1024 on MI355X) in flight, at 4 waves (see
+// mfma_column_split); the choice depends on the shape and width, never on the rows.
 template <int BITS>
-static hipError_t launch_mfma_b(int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
+static hipError_t launch_mfma_b(int waves, int split, int rows, int in_dim, int out_dim, const uint16_t* z,
                                 const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                                 hipStream_t stream) {
-  if (waves == 8) return launch_mfma_bw<BITS, 8>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-  return launch_mfma_bw<BITS, 4>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  if (waves == 8) return launch_mfma_bwh<BITS, 8, 1>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  const bool halves = split < 0 ? mfma_column_split(BITS, out_dim, waves) : split == 1;
+  if (halves) return launch_mfma_bwh<BITS, 4, 2>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  return launch_mfma_bwh<BITS, 4, 1>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
 }
 
 hipError_t launch_linear_mfma(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                               const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
-                              hipStream_t stream) {
+                              hipStream_t stream, int split) {
   if (rows == 0) return hipSuccess;
   switch (bits) {
-    case 2: return launch_mfma_b<2>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 3: return launch_mfma_b<3>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 4: return launch_mfma_b<4>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 5: return launch_mfma_b<5>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    case 6: return launch_mfma_b<6>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-    default: return launch_mfma_b<8>(waves, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 2: return launch_mfma_b<2>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 3: return launch_mfma_b<3>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 4: return launch_mfma_b<4>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 5: return launch_mfma_b<5>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    case 6: return launch_mfma_b<6>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+    default: return launch_mfma_b<8>(waves, split, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
   }
 }
 
