@@ -65,7 +65,7 @@ def _bucket(rows: int) -> int:
 def kernel_name(engine: str, rows: int) -> str:
     """The kernel that does the linear's work for `rows` rows on the LM head (first pass)."""
     if engine == "mfma":
-        return f"linear_mfma_kernel<{BITS}, 8>"
+        return f"linear_mfma_kernel<{BITS}, 8, 1>"
     if engine == "fused":
         import trellis_quantized_linear_tf_amd as tq
 
