@@ -93,14 +93,10 @@ hipError_t launch_linear_prompt(int bits, int waves, int rows, int in_dim, int o
 
 // The matrix-core linear at 4 waves runs its column-split form (twice the waves,
 // the same bits) where the first form would put fewer waves than SIMDs in flight.
-// Measured on 6144 x 25600 at 4 waves (us at 1 row, first form -> split): 2 bits
-// 30.9 -> 28.7, 4 bits 27.2 -> 26.0, 5 bits 51.4 -> 36.1, 6 bits 51.7 -> 34.2,
-// 8 bits 71.3 -> 38.1, but 3 bits 31.2 -> 36.0 (cause not found; bank
-// placement of the stage is not it), so 3 bits keeps the first form.
 constexpr long long kMfmaSplitBelowWaves = 1024;
 
 inline bool mfma_column_split(int bits, int out_dim, int waves) {
-  return waves == 4 && bits != 3 && (long long)(out_dim / 128) * waves < kMfmaSplitBelowWaves;
+  return waves == 4 && (long long)(out_dim / 128) * waves < kMfmaSplitBelowWaves;
 }
 
 // split: -1 = by mfma_column_split(), 0 = never, 1 = always at 4 waves.

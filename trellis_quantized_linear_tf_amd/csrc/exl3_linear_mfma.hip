@@ -196,6 +196,11 @@ __global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_p
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     issue(ring[(D + PF) % RING], zr[(D + PF) % RING], i + PF);
+    // In the split form (registers to spare) this keeps the loads at the top of
+    // the step: left to itself the scheduler sank them below the decode at 3
+    // bits, and the next step's stage write then waited for loads just issued.
+    // The first form keeps the scheduler's order: there the pin costs spills.
+    if constexpr (HALVES == 2) asm volatile("" ::: "memory");
     uint32_t kh[NT][CW];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
