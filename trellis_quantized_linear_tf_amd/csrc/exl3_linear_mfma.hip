@@ -119,7 +119,11 @@ __global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_p
   constexpr int NT = 8 / HALVES;  // tiles (MFMAs) per wave and pair
   constexpr int CW = khalf_raw_words<BITS>();
   constexpr int KW = khalf_words<BITS>();
-  constexpr int PF = prefetch_depth<BITS>() / 2 > 0 ? prefetch_depth<BITS>() / 2 : 1;  // pairs in flight
+  // Pairs in flight. The stage takes step i + 1's stream during step i, so PF
+  // pairs in flight give PF - 1 steps of cover: at least 2, except the 8-bit
+  // first form, where a second pair spills past 128 VGPRs (measured on the 8-bit
+  // LM head at 16 rows: 145 us against 140 with one pair; its many waves cover).
+  constexpr int PF = BITS == 8 && HALVES == 1 ? 1 : prefetch_depth<BITS>() / 2 > 2 ? prefetch_depth<BITS>() / 2 : 2;
   constexpr int RING = PF + 1;
   constexpr int RS = stage_row_words<BITS, HALVES>();  // stage words from tile row 2p to 2p + 1
   // Loads of a tile row's NT tiles (8 * BITS * NT words): LW lanes take PW contiguous dwords each.
