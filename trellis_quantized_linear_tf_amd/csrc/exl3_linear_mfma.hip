@@ -12,9 +12,11 @@
 //  - B (32 k x 16 n): lane l = 16g + n holds B[8g + t][n] = W[32p + 8g + t]
 //    [128 strip + 16m + n], t = 0..7: k-group g is tile row 2p + (g >> 1),
 //    k-half g & 1, of column n of tile m. These 8 values are 8 consecutive
-//    windows of the tile (value index 16n + 8(g & 1) + t), so the lane loads
-//    the 2 or 3 dwords that hold their 7*BITS + 16 bits (wrapping inside the
-//    tile), realigns them when the k-half does not start on a dword, and
+//    windows of the tile (value index 16n + 8(g & 1) + t). The wave brings
+//    each tile row in with one coalesced load (as the v_dot2 linear does) and
+//    writes it to a wave-private LDS stage one step ahead; the lane reads back
+//    the 2 or 3 dwords that hold its k-half's 7*BITS + 16 bits (wrapping inside
+//    the tile), realigns them when the k-half does not start on a dword, and
 //    decodes its B operand directly: no lane exchange, no zero padding;
 //  - A (16 rows x 32 k): lane 16g + r holds z[r][32p + 8g .. 32p + 8g + 7],
 //    one 16-byte load per lane per step (rows past the pass repeat its last
@@ -26,7 +28,8 @@
 // order (pairs ascending per wave, then the waves' sums in wave order), so a
 // row's bits never depend on the rows that share its launch. The order is a
 // different fixed one from the v_dot2 linear's: the two agree to the float64
-// gate, not bit for bit.
+// gate, not bit for bit. Narrow matrices at 4 waves run a column-split form
+// with the same bits (see linear_mfma_kernel's HALVES).
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
