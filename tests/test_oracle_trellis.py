@@ -48,6 +48,42 @@ def test_states_from_packed_symbols(bits):
     assert tr.tile_states_bitwise(words, bits) == expect
 
 
+def _planted_states(words, bits, plant):
+    """A copy of the word reader with one mistake planted: the second window of
+    each pair starts one bit late, or the last windows of a tile read past its
+    end instead of wrapping to its first word."""
+    nw = tr.tile_words(bits)
+    j = np.arange(256, dtype=np.int64)
+    p = j * bits + ((j & 1) if plant == "odd_window_one_bit_late" else 0)
+    w = np.concatenate([np.asarray(words, dtype=np.uint64), np.zeros(2, dtype=np.uint64)])
+    w0 = (p >> 5) % nw
+    w1 = (w0 + 1) % nw if plant != "no_wrap" else w0 + 1
+    pair = (w[w1] << np.uint64(32)) | w[w0]
+    return ((pair >> (p & 31).astype(np.uint64)) & np.uint64(0xFFFF)).astype(np.uint32)
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
+@pytest.mark.parametrize("plant", ["odd_window_one_bit_late", "no_wrap"])
+def test_planted_reader_mistakes_fail_the_reader_pins(bits, plant):
+    """The page's decode plant (the second window of each pair one bit off) and a
+    dropped tail wrap each fail the random-tile reader pins above: the bit-at-a-time
+    reader and the states rebuilt from packed symbols both disagree with them."""
+    words = synth.uniform_words(700 + bits, 8 * bits)
+    assert np.array_equal(_planted_states(words, bits, "none"), tr.tile_states(words, bits))  # the copy itself
+    assert list(_planted_states(words, bits, plant)) != tr.tile_states_bitwise(words, bits)
+    sym = (synth.splitmix64(710 + bits, 256) % np.uint64(1 << bits)).astype(np.uint64)
+    packed = synth.symbols_to_words(sym, bits)
+    assert not np.array_equal(_planted_states(packed, bits, plant), tr.tile_states(packed, bits))
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
+def test_constant_streams_cannot_see_the_window_plant(bits):
+    """Why the reader pins use random tiles: an all-ones stream gives 0xFFFF in every
+    window wherever it starts, so it passes the planted reader too."""
+    ones = np.full(8 * bits, 0xFFFFFFFF, dtype=np.uint32)
+    assert (_planted_states(ones, bits, "odd_window_one_bit_late") == 0xFFFF).all()
+
+
 def _hand_f16(bits16: int) -> Fraction:
     e = (bits16 >> 10) & 0x1F
     f = bits16 & 0x3FF
