@@ -445,10 +445,11 @@ def main() -> int:
 
     extra = {}
     if not args.no_r16:
-        # Both engines at 1 and 16 rows, same inputs and protocol (the headline is one of them).
+        # Both engines at 1, 2, 4, 8 and 16 rows (the metric's range), and the fused path at 1
+        # and 2, same inputs and protocol (the headline is one of them).
         table = {}
         for eng in ("dot2", "mfma", "fused"):
-            for r in ((1, 2) if eng == "fused" else (1, 16)):
+            for r in ((1, 2) if eng == "fused" else (1, 2, 4, 8, 16)):
                 t, l, _, _ = time_steps(torch, tq, trellis, xt[:r].contiguous(), suh_t, svh_t, args.steps,
                                         args.warmup, eng)
                 abr = algorithmic_bytes(r)
