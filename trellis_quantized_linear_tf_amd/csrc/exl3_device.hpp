@@ -193,23 +193,53 @@ __device__ __forceinline__ void decode_column(const uint32_t (&u)[column_words<B
 }
 
 // ---------------------------------------------------------------------------
+// The value lane ^ H holds, for the butterfly stages. DPP moves inside the
+// VALU where gfx950 has the pattern (H = 1, 2: quad_perm; H = 8: row_ror:8,
+// which is lane ^ 8 inside each 16-lane row), ds_swizzle's xor mode (no
+// address register) for H = 4 and 16, and a bpermute across the two 32-lane
+// halves for H = 32. Every lane of the wave must be active.
+template <int H>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (H == 1) {
+    r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (H == 2) {
+    r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (H == 8) {
+    r = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (H == 4 || H == 16) {
+    r = __builtin_amdgcn_ds_swizzle(i, 0x1F | (H << 10));  // and 0x1F, or 0, xor H
+  } else {
+    r = __builtin_bit_cast(int, __shfl_xor(v, H));
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// One stage h < 64: the pair (i, i + h) becomes (a + b, a - b) rounded to fp32;
+// a lane in the upper half of a pair computes fma(v, -1, partner) = partner - v
+// exactly as a subtraction would (v * -1 is exact, one rounding follows).
+template <int H>
+__device__ __forceinline__ void fwht_stage(float& v0, float& v1, int lane) {
+  const float sgn = (lane & H) ? -1.0f : 1.0f;
+  const float p0 = lane_xor<H>(v0);
+  const float p1 = lane_xor<H>(v1);
+  v0 = __builtin_fmaf(v0, sgn, p0);
+  v1 = __builtin_fmaf(v1, sgn, p1);
+}
+
 // 128-point butterflies on one wave: element e of the block lives in lane e % 64,
 // register e / 64 (v0 holds e = lane, v1 holds e = lane + 64). Stages run
-// h = 1, 2, ..., 64; in stage h the pair (i, i+h), i & h == 0, becomes
-// (a + b, a - b) rounded to fp32. Stages 1..32 pair lanes lane ^ h; a lane in
-// the upper half of a pair computes fma(v, -1, partner) = partner - v exactly as
-// a subtraction would (v * -1 is exact, one rounding follows). Stage 64 pairs
-// v0 with v1 inside the lane.
+// h = 1, 2, ..., 64; stages 1..32 pair lanes lane ^ h (fwht_stage); stage 64
+// pairs v0 with v1 inside the lane.
 __device__ __forceinline__ void fwht128_wave(float& v0, float& v1) {
   const int lane = __lane_id();
-#pragma unroll
-  for (int h = 1; h < kWave; h <<= 1) {
-    const float sgn = (lane & h) ? -1.0f : 1.0f;
-    const float p0 = __shfl_xor(v0, h);
-    const float p1 = __shfl_xor(v1, h);
-    v0 = __builtin_fmaf(v0, sgn, p0);
-    v1 = __builtin_fmaf(v1, sgn, p1);
-  }
+  fwht_stage<1>(v0, v1, lane);
+  fwht_stage<2>(v0, v1, lane);
+  fwht_stage<4>(v0, v1, lane);
+  fwht_stage<8>(v0, v1, lane);
+  fwht_stage<16>(v0, v1, lane);
+  fwht_stage<32>(v0, v1, lane);
   const float a = v0;
   const float b = v1;
   v0 = a + b;
