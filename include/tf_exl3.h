@@ -47,7 +47,7 @@ enum {
   TF_OK = 0,
   TF_E_BITS = -1,   /* bits not in {2, 3, 4, 5, 6, 8} */
   TF_E_SHAPE = -2,  /* a dimension < 128, not a multiple of 128, or a stream >= 4 GiB */
-  TF_E_ROWS = -3,   /* rows < 0 */
+  TF_E_ROWS = -3,   /* rows < 0, or more than 1048560 (65535 passes of 16; fewer for project) */
   TF_E_DTYPE = -4,  /* element type outside the table above */
   TF_E_NULL = -5,   /* a required pointer is NULL */
   TF_E_ALIGN = -6,  /* trellis or z not 16-byte aligned, or a row buffer not element-aligned */

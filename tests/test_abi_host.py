@@ -82,12 +82,19 @@ def test_plan_fields(lib):
 @pytest.mark.parametrize("args,code", [
     ((7, 1, 128, 128, 0), -1), ((1, 1, 128, 128, 0), -1),
     ((4, 1, 100, 128, 0), -2), ((4, 1, 128, 0, 0), -2), ((4, 1, 64, 128, 0), -2),
-    ((4, -1, 128, 128, 0), -3), ((4, 1, 128, 128, 6), -8), ((4, 1, 128, 128, 16), -8),
+    ((4, -1, 128, 128, 0), -3), ((4, 1048561, 128, 128, 0), -3), ((4, 1, 128, 128, 6), -8),
+    ((4, 1, 128, 128, 16), -8),
 ])
 def test_plan_refusals(lib, args, code):
     p = _lib.Plan()
     assert lib.tf_exl3_linear_plan(*args, ctypes.byref(p)) == code
     assert lib.tf_exl3_linear_plan(4, 1, 128, 128, 0, None) == -5
+
+
+def test_plan_accepts_the_largest_row_count(lib):
+    p = _lib.Plan()
+    assert lib.tf_exl3_linear_plan(4, 1048560, 128, 128, 0, ctypes.byref(p)) == 0
+    assert p.passes == 65535
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below is refused on the host
@@ -107,6 +114,7 @@ def test_linear_refusals(lib, entry):
     assert call(bits=9) == -1
     assert call(k=300) == -2
     assert call(rows=-2) == -3
+    assert call(rows=1048561) == -3  # more than 65535 passes of 16 rows
     assert call(dt=3) == -4
     assert call(z=None) == -5 and call(t=None) == -5 and call(s=None) == -5 and call(y=None) == -5
     assert call(z=FAKE + 8) == -6 and call(t=FAKE + 0x100004) == -6 and call(y=FAKE + 0x300002) == -6

@@ -15,6 +15,9 @@
 namespace {
 
 constexpr int kMaxRowsPerPass = 16;
+// Passes are the grid's second dimension (at most 65535 workgroups).
+constexpr int kMaxPasses = 65535;
+constexpr int kMaxRows = kMaxPasses * kMaxRowsPerPass;
 constexpr int kWaveEdgeColumns = 8192;
 
 int width_index(int bits) {
@@ -68,7 +71,7 @@ const char* tf_exl3_status_string(int status) {
     case TF_OK: return "ok";
     case TF_E_BITS: return "bits must be 2, 3, 4, 5, 6 or 8 (widthIndex)";
     case TF_E_SHAPE: return "in_dim and out_dim must be multiples of 128, and the stream under 4 GiB (fits)";
-    case TF_E_ROWS: return "rows must be >= 0";
+    case TF_E_ROWS: return "rows must be >= 0 and at most 1048560 (65535 passes of 16 rows)";
     case TF_E_DTYPE: return "element type must be TF_DT_F32, TF_DT_F16 or TF_DT_BF16";
     case TF_E_NULL: return "a required pointer is NULL";
     case TF_E_ALIGN: return "trellis and z must be 16-byte aligned and row buffers element-aligned";
@@ -84,7 +87,7 @@ int tf_exl3_linear_plan(int bits, int rows, int in_dim, int out_dim, int waves, 
   const int wi = width_index(bits);
   if (wi < 0) return TF_E_BITS;
   if (stream_bytes(bits, in_dim, out_dim) == 0) return TF_E_SHAPE;
-  if (rows < 0) return TF_E_ROWS;
+  if (rows < 0 || rows > kMaxRows) return TF_E_ROWS;
   const int w = plan_waves(out_dim, waves);
   if (w < 0) return TF_E_WAVES;
   tf_exl3_plan p;
@@ -227,6 +230,7 @@ int tf_exl3_project(int bits, int rows, int in_dim, int out_dim, const void* x, 
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return TF_E_DTYPE;
   const int pass_rows = tf_exl3::project_pass_rows(rows, plan.waves, in_dim);
   if (pass_rows == 0) return TF_E_SHAPE;
+  if (rows > 0 && (rows - 1) / pass_rows + 1 > kMaxPasses) return TF_E_ROWS;
   if (rows == 0) return TF_OK;
   if (x == nullptr || suh == nullptr || trellis == nullptr || svh == nullptr || y == nullptr) return TF_E_NULL;
   if (!aligned(x, elem_size(x_dtype)) || !aligned(suh, 2) || !aligned(trellis, 16) || !aligned(svh, 2) ||
