@@ -22,6 +22,8 @@ kernel's fp32 butterflies on the host. Readings:
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 from .numfmt import (
@@ -57,9 +59,24 @@ def finish_f32(acc32: np.ndarray, svh_bits: np.ndarray, out_dtype: str) -> np.nd
     return f32_to_output(v, out_dtype)
 
 
+def reference_threads() -> int:
+    """Host cores this process may run on (the threaded reference's default width)."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # platforms without CPU affinity
+        return max(1, os.cpu_count() or 1)
+
+
 def linear_f64(z_bits: np.ndarray, trellis: np.ndarray, bits: int, in_dim: int, out_dim: int,
-               svh_bits: np.ndarray, strips=None, strip_chunk: int = 32) -> np.ndarray:
-    """y64 [rows][128 * len(strips)] for the given 128-column strips (default: all)."""
+               svh_bits: np.ndarray, strips=None, strip_chunk: int = 32, threads: int = 1) -> np.ndarray:
+    """y64 [rows][128 * len(strips)] for the given 128-column strips (default: all).
+
+    The strips are taken in chunks of `strip_chunk`; each chunk unpacks its columns'
+    weights, sums z . W in float64 and finishes its blocks. With threads > 1 the chunks
+    are spread over a pool of that many threads (the page's float64 references split
+    their work by ranges of columns in the same way). A chunk's arithmetic does not
+    depend on which thread runs it, and every output keeps its own k order, so the
+    result is bit-identical to one thread's."""
     z_bits = np.atleast_2d(np.asarray(z_bits, dtype=np.uint16))
     assert z_bits.shape[1] == in_dim
     if strips is None:
@@ -67,12 +84,27 @@ def linear_f64(z_bits: np.ndarray, trellis: np.ndarray, bits: int, in_dim: int, 
     strips = np.asarray(strips, dtype=np.int64).reshape(-1)
     out = np.empty((z_bits.shape[0], BLOCK * strips.size), dtype=np.float64)
     svh_bits = np.asarray(svh_bits, dtype=np.uint16)
-    for i0 in range(0, strips.size, strip_chunk):
+
+    def chunk(i0: int) -> None:
         sel = strips[i0 : i0 + strip_chunk]
         w = unpack_columns(trellis, bits, in_dim, out_dim, strip_tile_cols(sel))
         acc = accumulate_f64(z_bits, w)
         cols = (BLOCK * sel[:, None] + np.arange(BLOCK)[None, :]).reshape(-1)
         out[:, BLOCK * i0 : BLOCK * (i0 + sel.size)] = finish_f64(acc, svh_bits[cols])
+
+    starts = range(0, strips.size, strip_chunk)
+    if threads <= 1 or len(starts) <= 1:
+        for i0 in starts:
+            chunk(i0)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    # One BLAS thread per worker: the pool is the parallelism.
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=threads) as pool:
+        for f in [pool.submit(chunk, i0) for i0 in starts]:
+            f.result()
     return out
 
 

@@ -123,12 +123,6 @@ def decode_states(states: np.ndarray) -> np.ndarray:
     return f64_to_f16_bits(codebook_exact(states))
 
 
-def decode_tile(words: np.ndarray, bits: int) -> np.ndarray:
-    """One tile -> [16 k][16 n] fp16 bits (R3)."""
-    st = tile_states(np.asarray(words).reshape(-1), bits)
-    return decode_states(st).reshape(16, 16).T.copy()
-
-
 # ---------------------------------------------------------------------------
 # Whole matrices (R4).
 

@@ -152,3 +152,56 @@ def test_float64_reference_does_not_depend_on_threads_chunks_or_rows():
     c = lin.linear_f64(z, stream, bits, k, n, svh, strip_chunk=3)
     d = np.concatenate([lin.linear_f64(z[i : i + 1], stream, bits, k, n, svh) for i in range(rows)])
     assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
+    # The threaded reference: strip chunks spread over pools of several widths.
+    for threads, chunk in ((2, 1), (3, 2), (lin.reference_threads(), 4)):
+        e = lin.linear_f64(z, stream, bits, k, n, svh, strip_chunk=chunk, threads=threads)
+        assert np.array_equal(a, e), (threads, chunk)
+
+
+def test_threaded_reference_keeps_strip_order():
+    """A strip list out of order (and with repeats) gives each strip's block where the
+    list puts it, threaded or not: the pool writes every chunk to its own columns."""
+    bits, k, n = 3, 256, 1024
+    stream = synth.trellis_words(74, bits, k, n)
+    z = synth.rows(75, 2, k, "f16", 1.0)
+    svh = synth.signs(76, n)
+    full = lin.linear_f64(z, stream, bits, k, n, svh)
+    order = [7, 0, 3, 3, 5, 1]
+    y = lin.linear_f64(z, stream, bits, k, n, svh, strips=order, strip_chunk=1, threads=4)
+    assert np.array_equal(y, full[:, lin.strip_columns(order)])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_ulp_is_the_rounding_bound_exactly(dtype):
+    """half_ulp(v) is the largest error of rounding v to the output type: midpoints
+    between neighbouring values reach it (so a full-ulp allowance would be caught),
+    and no value exceeds it. The rounding comes from numpy (fp16) and torch (bf16),
+    not from the oracle."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    if dtype == "f16":
+        lo = rng.integers(0x0400, 0x7BFF, 4000).astype(np.uint16)  # normal, below the largest
+        a = lo.view(np.float16).astype(np.float64)
+        b = (lo + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+        rnd = lambda v: v.astype(np.float16).astype(np.float64)
+    else:
+        lo = rng.integers(0x0080, 0x7F7F, 4000).astype(np.uint32)
+        a = (lo << 16).view(np.float32).astype(np.float64)
+        b = ((lo + 1) << 16).view(np.float32).astype(np.float64)
+        rnd = lambda v: torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    for sign in (1.0, -1.0):
+        mid = sign * (a + b) / 2  # exact in float64
+        assert np.array_equal(lin.half_ulp(mid, dtype), np.abs(rnd(mid) - mid))
+        off = sign * (a + 0.3 * (b - a))
+        assert np.all(np.abs(rnd(off) - off) <= lin.half_ulp(off, dtype))
+
+
+def test_gate_charges_a_one_ulp_miss_half_an_ulp():
+    """An fp16 output one ulp from y64 = 1 is charged exactly half an ulp (2^-11):
+    the allowance is half an ulp, not a whole one."""
+    y64 = np.array([1.0, -1.0])
+    y = np.array([0x3C01, 0xBC00], dtype=np.uint16)  # 1 + 2^-10, -1
+    assert lin.gate_error(y, "f16", y64) == 2.0 ** -11
+    yb = np.array([0x3F81, 0xBF80], dtype=np.uint16)  # bf16 1 + 2^-7, -1
+    assert lin.gate_error(yb, "bf16", y64) == 2.0 ** -8
