@@ -148,6 +148,62 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+# Argument checks. The C ABI sees plain pointers, not buffer sizes, so a short
+# stream or a wrong-shaped output would become an out-of-bounds device access,
+# and an fp32 tensor passed where fp16 bits are read would be misread silently.
+# Every wrapper checks element types, shapes and byte sizes first (these checks
+# need no GPU), then that all tensors are contiguous and on one GPU.
+
+
+def _half_bits_dtypes():
+    torch = _torch()
+    return (torch.float16, torch.int16)
+
+
+def _row_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(name: str, t, dtypes=None, shape=None, nbytes=None) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must have element type {' or '.join(map(str, dtypes))}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if nbytes is not None and _nbytes(t) != nbytes:
+        raise ValueError(f"{name} must hold {nbytes} bytes, not {_nbytes(t)}")
+
+
+def _need_2d(name: str, t) -> tuple:
+    if t is None or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor [rows][dim]")
+    return tuple(t.shape)
+
+
+def _stream_bytes(bits: int, in_dim: int, out_dim: int) -> int | None:
+    """Stream size the library expects, or None where the library refuses the shape
+    (it then returns its status before any launch)."""
+    n = trellis_bytes(bits, in_dim, out_dim)
+    return n if n > 0 else None
+
+
+def _same_gpu(*tensors) -> None:
+    ts = [t for t in tensors if t is not None]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if len({t.device for t in ts}) > 1:
+        raise ValueError("all tensors must be on one GPU")
+
+
 def _stream(t) -> int:
     return _torch().cuda.current_stream(t.device).cuda_stream
 
@@ -155,7 +211,12 @@ def _stream(t) -> int:
 def rot_in(x, suh, z=None):
     """z[rows][in_dim] fp16 = rot_in(x, suh); x is fp32/fp16/bf16 [rows][in_dim], suh fp16 [in_dim]."""
     torch = _torch()
-    rows, in_dim = x.shape
+    rows, in_dim = _need_2d("x", x)
+    _need("x", x, _row_dtypes())
+    _need("suh", suh, _half_bits_dtypes(), (in_dim,))
+    if z is not None:
+        _need("z", z, _half_bits_dtypes(), (rows, in_dim))
+    _same_gpu(x, suh, z)
     if z is None:
         z = torch.empty((rows, in_dim), dtype=torch.float16, device=x.device)
     _check(load().tf_exl3_rot_in(_ptr(x), _dt_code(x.dtype), _ptr(suh), _ptr(z), rows, in_dim, _stream(x)))
@@ -165,6 +226,20 @@ def rot_in(x, suh, z=None):
 ENGINES = ("dot2", "mfma", "prompt", "strips")
 
 
+def _check_linear_args(z, trellis, svh, bits: int, out_dim: int, y, out_dtype) -> tuple:
+    """Shapes, element types and the stream's size of a linear call; returns (rows, in_dim)."""
+    rows, in_dim = _need_2d("z", z)
+    _need("z", z, _half_bits_dtypes())
+    _need("trellis", trellis, nbytes=_stream_bytes(bits, in_dim, out_dim))
+    _need("svh", svh, _half_bits_dtypes(), (out_dim,))
+    if y is not None:
+        _need("y", y, _row_dtypes(), (rows, out_dim))
+    elif out_dtype is not None and out_dtype not in _row_dtypes():
+        raise ValueError(f"out_dtype must be one of {_row_dtypes()}")
+    _same_gpu(z, trellis, svh, y)
+    return rows, in_dim
+
+
 def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0,
            engine: str = "dot2"):
     """y[rows][out_dim] = the trellis linear of fp16 z [rows][in_dim] (trellis: uint8/int32 stream).
@@ -172,11 +247,11 @@ def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, wav
     tf_exl3_linear_prompt (32-row passes, bit-equal to "dot2") and "strips"
     tf_exl3_linear_strips (trellis in the strips layout, see repack_strips)."""
     torch = _torch()
-    rows, in_dim = z.shape
-    if y is None:
-        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
     if engine not in ENGINES:
         raise ValueError(f"engine must be one of {ENGINES}")
+    rows, in_dim = _check_linear_args(z, trellis, svh, bits, out_dim, y, out_dtype)
+    if y is None:
+        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
     lib = load()
     fn = {"dot2": lib.tf_exl3_linear, "mfma": lib.tf_exl3_linear_mfma, "prompt": lib.tf_exl3_linear_prompt,
           "strips": lib.tf_exl3_linear_strips}[engine]
@@ -188,6 +263,11 @@ def linear(z, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, wav
 def repack_strips(trellis, bits: int, in_dim: int, out_dim: int, out=None):
     """The strips-layout image of a tile-layout stream (tf_exl3_repack_strips)."""
     torch = _torch()
+    n = _stream_bytes(bits, in_dim, out_dim)
+    _need("trellis", trellis, nbytes=n)
+    if out is not None:
+        _need("out", out, nbytes=n)
+    _same_gpu(trellis, out)
     if out is None:
         out = torch.empty_like(trellis)
     _check(load().tf_exl3_repack_strips(bits, in_dim, out_dim, _ptr(trellis), _ptr(out), _stream(trellis)))
@@ -197,7 +277,16 @@ def repack_strips(trellis, bits: int, in_dim: int, out_dim: int, out=None):
 def project(x, suh, trellis, svh, bits: int, out_dim: int, y=None, out_dtype=None, waves: int = 0):
     """y = linear(rot_in(x)) in one launch (bit-identical to rot_in then linear with engine "dot2")."""
     torch = _torch()
-    rows, in_dim = x.shape
+    rows, in_dim = _need_2d("x", x)
+    _need("x", x, _row_dtypes())
+    _need("suh", suh, _half_bits_dtypes(), (in_dim,))
+    _need("trellis", trellis, nbytes=_stream_bytes(bits, in_dim, out_dim))
+    _need("svh", svh, _half_bits_dtypes(), (out_dim,))
+    if y is not None:
+        _need("y", y, _row_dtypes(), (rows, out_dim))
+    elif out_dtype is not None and out_dtype not in _row_dtypes():
+        raise ValueError(f"out_dtype must be one of {_row_dtypes()}")
+    _same_gpu(x, suh, trellis, svh, y)
     if y is None:
         y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=x.device)
     _check(load().tf_exl3_project(bits, rows, in_dim, out_dim, _ptr(x), _dt_code(x.dtype), _ptr(suh),
@@ -214,6 +303,7 @@ def project_pass_rows(rows: int, in_dim: int, out_dim: int, waves: int = 0) -> i
 def debug_decode_states(states):
     """fp16 weights (as int16 bits) of uint16 states given as an int16/int32 tensor of 16-bit values."""
     torch = _torch()
+    _same_gpu(states)
     s = states.to(torch.int16) if states.dtype != torch.int16 else states
     w = torch.empty_like(s)
     _check(load().tf_exl3_debug_decode_states(_ptr(s), _ptr(w), s.numel(), _stream(s)))
@@ -223,6 +313,8 @@ def debug_decode_states(states):
 def debug_decode_tiles(trellis, bits: int, in_dim: int, out_dim: int):
     """W[in_dim][out_dim] as fp16 decoded by the linear's own decode path."""
     torch = _torch()
+    _need("trellis", trellis, nbytes=_stream_bytes(bits, in_dim, out_dim))
+    _same_gpu(trellis)
     w = torch.empty((in_dim, out_dim), dtype=torch.float16, device=trellis.device)
     _check(load().tf_exl3_debug_decode_tiles(bits, in_dim, out_dim, _ptr(trellis), _ptr(w), _stream(trellis)))
     return w
@@ -233,7 +325,7 @@ def debug_linear_split(z, trellis, svh, bits: int, out_dim: int, split: int, y=N
     """tf_exl3_linear with every launch forced to the regular (split 0) or the
     column-split (split 1) kernels (tf_exl3_debug_linear_split)."""
     torch = _torch()
-    rows, in_dim = z.shape
+    rows, in_dim = _check_linear_args(z, trellis, svh, bits, out_dim, y, out_dtype)
     if y is None:
         y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
     _check(load().tf_exl3_debug_linear_split(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y),
@@ -243,13 +335,19 @@ def debug_linear_split(z, trellis, svh, bits: int, out_dim: int, split: int, y=N
 
 def calib_copy(src, dst, blocks: int = 2048):
     """dst <- src byte for byte (both contiguous device tensors of equal byte size)."""
-    nbytes = src.numel() * src.element_size()
-    assert dst.numel() * dst.element_size() == nbytes
+    nbytes = _nbytes(src)
+    _need("dst", dst, nbytes=nbytes)
+    _same_gpu(src, dst)
     _check(load().tf_exl3_calib_copy(_ptr(src), _ptr(dst), nbytes, blocks, _stream(src)))
 
 
 def calib_stream_read(src, out):
     """Reads all of src; out is an int32 tensor of blocks * 256 entries."""
-    nbytes = src.numel() * src.element_size()
+    torch = _torch()
+    nbytes = _nbytes(src)
+    _need("out", out, (torch.int32,))
+    if out.numel() < 256 or out.numel() % 256:
+        raise ValueError("out must hold a positive multiple of 256 int32 words (one per thread)")
     blocks = out.numel() // 256
+    _same_gpu(src, out)
     _check(load().tf_exl3_calib_stream_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(src)))
