@@ -170,7 +170,9 @@ int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint1
 
 /*
  * project: rot_in and the linear in one launch, y = linear(rot_in(x)).
- * Every workgroup rotates its pass's rows into LDS with the same arithmetic as
+ * Source: the same page, "What this changes": the projection is the two calls in
+ * sequence, rot_in's fp16 rows feeding the linear; this entry runs both as one
+ * launch with rot_in's arithmetic unchanged. Every workgroup rotates its pass's rows into LDS with the same arithmetic as
  * tf_exl3_rot_in and then runs tf_exl3_linear's own tile-row walk, so y is bit
  * for bit what tf_exl3_rot_in followed by tf_exl3_linear gives, with one launch
  * and no z buffer. Each workgroup recomputes the rotation of its rows (about 6%
@@ -188,10 +190,18 @@ int tf_exl3_project(int bits, int rows, int in_dim, int out_dim, const void* x, 
                     int y_dtype, int waves, void* stream);
 
 /* Rows per pass tf_exl3_project uses for these arguments (host only), or a refusal:
- * TF_E_SHAPE if even one row does not fit, TF_E_ROWS, TF_E_WAVES. */
+ * TF_E_SHAPE if even one row does not fit, TF_E_ROWS, TF_E_WAVES. The pass size is
+ * the single launch's own planning (its LDS holds a pass's rotated rows); the rows
+ * per pass of the page's linear ("What this changes": 1 to 16 rows a pass) bound it. */
 int tf_exl3_project_pass_rows(int rows, int in_dim, int out_dim, int waves);
 
-/* Launch plan the linear would use (host only; no GPU needed). */
+/*
+ * Launch plan the linear would use (host only; no GPU needed). Source: the same
+ * page, "What this changes" (the launches refuse the shapes they cannot run
+ * ("fits"), map the width to a kernel ("widthIndex") and choose the wave count,
+ * with no K split, all host-tested) and "Kernel contract" (the plan's 8-wave edge:
+ * 8192 output columns by 1024 run on 8 waves, 8064 by 1024 on 4).
+ */
 typedef struct {
   int width_index;    /* position of bits in {2, 3, 4, 5, 6, 8} */
   int waves;          /* waves per block */
@@ -214,14 +224,22 @@ typedef struct {
 int tf_exl3_linear_plan(int bits, int rows, int in_dim, int out_dim, int waves,
                         tf_exl3_plan* out);
 
-/* Bytes of a trellis stream: in_dim * out_dim * bits / 8 (0 for a refused shape). */
+/* Bytes of a trellis stream: in_dim * out_dim * bits / 8 (0 for a refused shape).
+ * Source: the same page, "Kernel contract": the linear's static LDS records hold
+ * eight tiles per wave, 32 * bits bytes per 16 x 16 tile, i.e. bits bits per weight. */
 size_t tf_exl3_trellis_bytes(int bits, int in_dim, int out_dim);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL). The refusals are the planner's
+ * ("What this changes": fits, widthIndex, waves) and this interface's own pointer,
+ * alignment and overlap checks. */
 const char* tf_exl3_status_string(int status);
 
 /*
  * Test entry points. They run the same device decode functions as the linear.
+ * Source: the same page, "Checks on this head": the linear's kernel test decodes
+ * every width's weights bit for bit as the format's unpack does, and its window
+ * test compares a row's bits across launches; these entries expose the decode
+ * and the variant choice so the tests can check both against the oracle.
  *
  * debug_decode_states: w[i] = codebook(states[i]) as fp16 bits, i < n.
  *   states, w: device arrays of n uint16; n >= 0.
@@ -239,7 +257,9 @@ int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t
                                uint16_t* w, void* stream);
 
 /*
- * Calibration entry points for measurement (not part of the projection). Both
+ * Calibration entry points for measurement (not part of the projection, and
+ * defined by no page: they give the device's own copy and read rates, against
+ * which the linear's HBM traffic counters and bandwidth are scaled). Both
  * move 16 bytes per lane in wave-contiguous 1 KiB runs, the access form of the
  * linear's weight stream.
  *

@@ -1,11 +1,13 @@
 // The trellis linear: 1..16 decode rows per pass, and the prompt path's 32-row
 // passes.
 //
-// TensorFold pull request "hip exl3: the input rotation and trellis linear for
-// decode rows", "What this changes": a lane decodes its 16 x 16 tile values with
-// one fp16 fma each; a row's sums are v_dot2_f32_f16 chains in a fixed order, so
-// a row's bits do not depend on the rows sharing its launch; the waves' partial
-// sums, the output rotation and svh finish the block; no K split, no bias.
+// Source: TensorFold pull request "hip exl3: the input rotation and trellis
+// linear for decode rows", section "What this changes". Each weight costs one
+// fp16 fused multiply-add in the codebook; every output's sum over k is a chain
+// of v_dot2_f32_f16 whose order is fixed by the shape alone, which is what keeps
+// an output row's bits independent of its launch-mates. After the k sums, the
+// per-wave partials are added, the 128-point output rotation and the svh scale
+// are applied. The k range is never split across workgroups and there is no bias.
 //
 // Work layout on gfx950:
 //  - one workgroup per (128-column strip, pass of rows);

@@ -1,9 +1,10 @@
 // Pieces shared by the linear kernels: the stream share load, the output
 // store, and the strip finish (cross-wave sums, output butterflies, scale, svh).
 //
-// TensorFold pull request "hip exl3: the input rotation and trellis linear for
-// decode rows", "What this changes": the waves' sums, the output rotation and
-// svh follow the finish of the reference path.
+// Source: TensorFold pull request "hip exl3: the input rotation and trellis
+// linear for decode rows", section "What this changes" (the block's finish: the
+// wave partials are added, then rotated, scaled and multiplied by svh in the
+// same order as the input rotation's arithmetic).
 #pragma once
 
 #include <type_traits>
