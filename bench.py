@@ -1,14 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of the EXL3 decode-row projection on one MI355X.
 
-Workload: the LM head, 5120 -> 129,280 at 4 bits, fp16 input rows ~N(0, 0.5),
-+-1 suh/svh, fp32 logits. One step is rot_in on the rows followed by the trellis
-linear: the whole path, on inputs already resident in HBM. The headline value is
-one row per step (a decode token); a second timed region runs 16 rows per step.
+Headline workload: the LM head, 5120 -> 129,280 at 4 bits, fp16 input rows
+~N(0, 0.5), +-1 suh/svh, fp32 logits. One step is rot_in on the rows followed by
+the trellis linear: the whole path, on inputs already resident in HBM. The
+headline value is one row per step (a decode token); further regions run 2, 4, 8
+and 16 rows on both engines, and every workload of the test suite.
 
-The weight stream is 331 MB; steps alternate between two copies of it (662 MB,
-more than the 256 MB Infinity Cache and the L2s together), so no step reads a
-stream that the previous step left in a cache.
+Cache protocol: each timed region rotates through copies of its weight stream
+that together exceed ROTATE_BYTES (1.2 GB: more than the 256 MB Infinity Cache and
+the L2s together), taking consecutive steps from copies written longest ago, so
+no step reads a stream that an earlier step or the setup left in a cache.
 
 Prints one JSON line (see the fields at the end of main()).
 """
@@ -18,8 +20,10 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import re
+import math
 import os
+import re
+import subprocess
 import sys
 import time
 from pathlib import Path
@@ -41,9 +45,12 @@ DOT_OPS_PER_WEIGHT_ROW = 0.5
 FINISH_OPS_PER_OUTPUT = 9  # cross-wave sums, butterflies, scale, svh per output
 BITS, IN_DIM, OUT_DIM = 4, 5120, 129280
 WORKLOAD_ID = 3  # seeds: 1000 * workload + stream
-CPU_SAMPLE_STRIPS = 384  # about 10-15 s of oracle work on one core
+ROWS_PER_PASS = 16
+ROTATE_BYTES = 1_200_000_000
 WARMUP_S = 0.5
+ROW_COUNTS = (1, 2, 4, 8, 16)
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_linear_lmhead_4bit.json"
+RESOURCES_FILE = ROOT / "trellis_quantized_linear_tf_amd" / "libtf_exl3.resources.json"
 # The sources each engine's linear kernel is built from (the traffic record is keyed on them).
 _COMMON = ["exl3_device.hpp", "exl3_strip.hpp"]
 ENGINE_SOURCES = {
@@ -74,7 +81,6 @@ def kernel_name(engine: str, rows: int) -> str:
         return f"linear_lds_kernel<{BITS}, 8, 32>"
     b = _bucket(min(rows, 16))
     return f"linear_kernel<{BITS}, 8, {b}>" if b <= 4 else f"linear_lds_kernel<{BITS}, 8, {b}>"
-PROMPT_ROWS = 128
 
 
 def code_text(src: str) -> str:
@@ -93,21 +99,25 @@ def kernel_source_hash(engine: str, read=None) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(rows: int) -> dict:
-    """Bytes the linear must move per launch: the stream, z, y, svh."""
-    stream = IN_DIM * OUT_DIM * BITS // 8
-    z = rows * IN_DIM * 2
-    y = rows * OUT_DIM * 4
-    svh = OUT_DIM * 2
-    return {"stream": stream, "total": stream + z + y + svh}
+def passes(rows: int) -> int:
+    return max(1, math.ceil(rows / ROWS_PER_PASS))
 
 
-def algorithmic_valu_ops(engine: str, rows: int) -> float:
-    """VALU lane-instructions the linear needs per launch: the decode of every weight,
-    the v_dot2 sums of every row (on the matrix cores for the mfma engine), the finish."""
-    weights = IN_DIM * OUT_DIM
+def algorithmic_bytes(rows: int, bits: int = BITS, k: int = IN_DIM, n: int = OUT_DIM, y_size: int = 4) -> dict:
+    """Bytes one launch of the linear must move: the stream once per pass of 16 rows,
+    z, y and svh (suh belongs to rot_in)."""
+    stream = k * n * bits // 8
+    total = passes(rows) * stream + rows * k * 2 + rows * n * y_size + 2 * n
+    return {"stream": stream, "total": total}
+
+
+def algorithmic_valu_ops(engine: str, rows: int, k: int = IN_DIM, n: int = OUT_DIM) -> float:
+    """VALU lane-instructions the linear needs per launch (4-bit decode): the decode of
+    every weight once per pass, the v_dot2 sums of every row (on the matrix cores for the
+    mfma engine), the finish."""
+    weights = k * n
     dot = 0.0 if engine == "mfma" else DOT_OPS_PER_WEIGHT_ROW * rows
-    return weights * (DECODE_OPS_PER_WEIGHT + dot) + rows * OUT_DIM * FINISH_OPS_PER_OUTPUT
+    return weights * (DECODE_OPS_PER_WEIGHT * passes(rows) + dot) + rows * n * FINISH_OPS_PER_OUTPUT
 
 
 def load_traffic(engine: str, rows: int):
@@ -121,7 +131,22 @@ def load_traffic(engine: str, rows: int):
     return rec.get("per_launch_bytes", {}).get(key)
 
 
-def make_inputs(torch, dev, rows: int, copies: int):
+def rotating_copies(torch, dev, stream_np, min_bytes: int = ROTATE_BYTES):
+    """Views of ceil(min_bytes / stream bytes) (at least 2) copies of the stream in one
+    device buffer, in the order they were written."""
+    import numpy as np
+
+    words = stream_np.size
+    nbytes = words * 4
+    copies = max(2, math.ceil(min_bytes / nbytes))
+    src = torch.from_numpy(stream_np.view(np.int32)).to(dev)
+    buf = torch.empty((copies, words), dtype=torch.int32, device=dev)
+    buf.copy_(src.unsqueeze(0).expand(copies, words))
+    del src
+    return [buf[i] for i in range(copies)]
+
+
+def make_inputs(torch, dev, rows: int):
     import numpy as np
 
     import synth
@@ -130,36 +155,46 @@ def make_inputs(torch, dev, rows: int, copies: int):
     x = synth.rows(synth.seed_for(WORKLOAD_ID, synth.STREAM_ROWS), rows, IN_DIM, "f16", 0.5)
     suh = synth.signs(synth.seed_for(WORKLOAD_ID, synth.STREAM_SUH), IN_DIM)
     svh = synth.signs(synth.seed_for(WORKLOAD_ID, synth.STREAM_SVH), OUT_DIM)
-    t_host = torch.from_numpy(stream.view(np.int32))
-    trellis = [t_host.to(dev) for _ in range(copies)]
+    trellis = rotating_copies(torch, dev, stream)
     xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
     suh_t = torch.from_numpy(suh.view(np.int16)).to(dev).view(torch.float16)
     svh_t = torch.from_numpy(svh.view(np.int16)).to(dev).view(torch.float16)
     return trellis, xt, suh_t, svh_t, (stream, x, suh, svh)
 
 
-def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, engine: str = "dot2"):
+class Shape:
+    """The linear's arguments that stay fixed in a timed region."""
+
+    def __init__(self, bits=BITS, k=IN_DIM, n=OUT_DIM, waves=0, y_dtype=None):
+        self.bits, self.k, self.n, self.waves, self.y_dtype = bits, k, n, waves, y_dtype
+
+
+def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, engine: str = "dot2",
+               shape: Shape | None = None):
     """Warm up, then two timed regions of exactly `steps` steps each: the steps alone
     (events only before and after: ms per step), then the same steps with HIP events
-    around every launch of the linear's kernel, on its stream (its duration: the
-    events themselves cost the step a few microseconds, so they stay out of the first
-    region)."""
+    around every launch of the linear's kernel, on the stream it is launched on (its
+    duration: the events themselves cost the step a few microseconds, so they stay out
+    of the first region). Step i reads stream copy (warmup + i) mod copies, so the
+    timed steps start on the copies written longest ago."""
+    sh = shape or Shape()
     rows = xt.shape[0]
-    z = torch.empty((rows, IN_DIM), dtype=torch.float16, device=xt.device)
-    y = torch.empty((rows, OUT_DIM), dtype=torch.float32, device=xt.device)
+    z = torch.empty((rows, sh.k), dtype=torch.float16, device=xt.device)
+    y = torch.empty((rows, sh.n), dtype=sh.y_dtype or torch.float32, device=xt.device)
     copies = len(trellis)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        t = trellis[i % copies]
         if engine == "fused":
             if ev:
                 ev[0].record(stream)
-            tq.project(xt, suh_t, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y)
+            tq.project(xt, suh_t, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves)
         else:
             tq.rot_in(xt, suh_t, z)
             if ev:
                 ev[0].record(stream)
-            tq.linear(z, trellis[i % copies], svh_t, BITS, OUT_DIM, y=y, engine=engine)
+            tq.linear(z, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves, engine=engine)
         if ev:
             ev[1].record(stream)
 
@@ -171,21 +206,22 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, en
         i += 1
         if i % 64 == 0:
             torch.cuda.synchronize()
+    base = i
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for i in range(steps):
-        step(i)
+    for j in range(steps):
+        step(base + j)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        step(i, ev[i])
+    for j in range(steps):
+        step(base + steps + j, ev[j])
     torch.cuda.synchronize()
     lin_ms = [a.elapsed_time(b) for a, b in ev]
     return total_ms, lin_ms, wall, y
@@ -197,29 +233,41 @@ def _percentiles(v):
 
 
 def cpu_baseline(host_inputs, rows: int) -> dict:
-    """The oracle (rot_in fp32 steps + float64 linear) on a bounded sample of strips."""
+    """The oracle as it stands, timed on this host: its float64 linear threaded over
+    strips on the host cores (the threaded reference, bit-identical to one thread),
+    and rot_in's fp32 steps separately (one thread: a row is 40 blocks)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import linear as lin
     from oracle import rotation as rot
 
     stream, x, suh, svh = host_inputs
-    strips = np.arange(CPU_SAMPLE_STRIPS)
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        z = rot.rot_in(x[:rows], "f16", suh)
-        lin.linear_f64(z, stream, BITS, IN_DIM, OUT_DIM, svh, strips=strips)
-        dt = time.perf_counter() - t0
-    sample_stream_bytes = IN_DIM * 128 * CPU_SAMPLE_STRIPS * BITS // 8
+    threads = lin.reference_threads()
+    n_strips = OUT_DIM // 128
+    sample = n_strips if threads >= 8 else 384  # about 10-30 s of CPU work either way
+    strips = np.arange(sample)
+    z = rot.rot_in(x[:rows], "f16", suh)
+    t0 = time.perf_counter()
+    lin.linear_f64(z, stream, BITS, IN_DIM, OUT_DIM, svh, strips=strips, threads=threads)
+    dt = time.perf_counter() - t0
+    reps, t1 = 0, time.perf_counter()
+    while reps < 3 or time.perf_counter() - t1 < 0.5:
+        rot.rot_in(x[:rows], "f16", suh)
+        reps += 1
+    rot_s = (time.perf_counter() - t1) / reps
+    sample_stream_bytes = IN_DIM * 128 * sample * BITS // 8
+    linear_s = dt * n_strips / sample
     return {
         "value": round(sample_stream_bytes / dt / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{rows} row, {CPU_SAMPLE_STRIPS} of 1010 strips ({IN_DIM} x {128 * CPU_SAMPLE_STRIPS} weights), "
-                  f"rot_in + float64 linear, {dt:.1f} s",
-        "rows_per_s": round(rows * CPU_SAMPLE_STRIPS / 1010 / dt, 6),
+        "sample": f"{rows} fp16 row(s): float64 linear over {sample} of {n_strips} strips "
+                  f"({IN_DIM} x {128 * sample} weights) on {threads} threads, {dt:.1f} s; "
+                  f"rot_in (fp32 steps, 1 thread) timed alone",
+        "rows_per_s": round(rows / (linear_s + rot_s), 6),
+        "linear_s_per_step": round(linear_s, 4),
+        "rot_in": {"s_per_step": round(rot_s, 6), "rows_per_s": round(rows / rot_s, 2), "cores": 1},
     }
 
 
@@ -304,18 +352,19 @@ def ingest_counters(base: Path) -> dict:
 
 # The test suite's workloads (shape, widths, rows, input and output types, waves).
 CONFIGS = [
-    ("indexer wk 512->128", 1, 512, 128, (4,), (1,), "f16", "f32", 0),
-    ("Engram wkv 6144->25600", 2, 6144, 25600, (3, 4), (1, 2, 8, 16), "bf16", "f16", 4),
-    ("LM head 5120->129280", 3, 5120, 129280, (4,), (1, 16), "f16", "f32", 0),
-    ("width sweep 6144->25600", 4, 6144, 25600, (2, 3, 4, 5, 6, 8), (64,), "f16", "f32", 8),
-    ("stress LM head 8-bit", 5, 5120, 129280, (8,), (64,), "bf16", "f32", 0),
+    ("indexer wk 512->128", 1, 512, 128, (4,), (1,), "f16", "f32", 0, 1.0),
+    ("Engram wkv 6144->25600", 2, 6144, 25600, (3, 4), (1, 2, 8, 16), "bf16", "f16", 4, 1.0),
+    ("LM head 5120->129280", 3, 5120, 129280, (4,), (1, 16), "f16", "f32", 0, 0.5),
+    ("width sweep 6144->25600", 4, 6144, 25600, (2, 3, 4, 5, 6, 8), (64,), "f16", "f32", 8, 1.0),
+    ("stress LM head 8-bit", 5, 5120, 129280, (8,), (64,), "bf16", "f32", 0, 1.0),
 ]
+_TDT = {"f32": 4, "f16": 2, "bf16": 2}
 
 
-def time_configs(torch, tq, steps: int) -> list:
-    """Step time (rot_in + linear) of every workload, both engines, HIP events around
-    the steps only, median of five blocks (one stream copy: these shapes' streams are not all larger than the
-    Infinity Cache, so the small ones may run from it)."""
+def time_configs(torch, tq, steps: int, warmup: int) -> list:
+    """Every workload on both engines under the bench's protocol (rotating stream copies
+    over 1.2 GB, warm-up, ms per step from a region without per-launch events, the
+    linear's kernel time from events around each launch)."""
     import numpy as np
 
     import synth
@@ -323,52 +372,74 @@ def time_configs(torch, tq, steps: int) -> list:
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     out = []
-    for name, wid, k, n, widths, row_counts, xdt, ydt, waves in CONFIGS:
+    for name, wid, k, n, widths, row_counts, xdt, ydt, waves, sigma in CONFIGS:
         suh = torch.from_numpy(synth.signs(synth.seed_for(wid, synth.STREAM_SUH), k).view(np.int16)).to(dev)
         svh = torch.from_numpy(synth.signs(synth.seed_for(wid, synth.STREAM_SVH), n).view(np.int16)).to(dev)
+        suh, svh = suh.view(torch.float16), svh.view(torch.float16)
         for bits in widths:
-            stream = synth.trellis_words(synth.seed_for(wid, synth.STREAM_TRELLIS), bits, k, n)
-            tt = torch.from_numpy(stream.view(np.int32)).to(dev)
+            stream = synth.trellis_words(synth.seed_for(wid, synth.STREAM_TRELLIS) + 10 * bits, bits, k, n)
+            copies = rotating_copies(torch, dev, stream)
             for rows in row_counts:
-                x = synth.rows(synth.seed_for(wid, synth.STREAM_ROWS), rows, k, xdt, 1.0)
+                x = synth.rows(synth.seed_for(wid, synth.STREAM_ROWS), rows, k, xdt, sigma)
                 xt = torch.from_numpy(x.view(np.int16 if xdt != "f32" else np.float32)).to(dev)
                 if xdt != "f32":
                     xt = xt.view(tdt[xdt])
-                z = torch.empty((rows, k), dtype=torch.float16, device=dev)
-                y = torch.empty((rows, n), dtype=tdt[ydt], device=dev)
+                shape = Shape(bits, k, n, waves, tdt[ydt])
+                ab = algorithmic_bytes(rows, bits, k, n, _TDT[ydt])
                 rec = {"workload": name, "bits": bits, "rows": rows, "x": xdt, "y": ydt,
-                       "waves": tq.linear_plan(bits, rows, k, n, waves)["waves"]}
+                       "waves": tq.linear_plan(bits, rows, k, n, waves)["waves"], "stream_copies": len(copies),
+                       "bytes_per_launch": ab["total"]}
                 for engine in ("dot2", "mfma"):
-                    def step():
-                        tq.rot_in(xt, suh, z)
-                        tq.linear(z, tt, svh, bits, n, y=y, waves=waves, engine=engine)
-
-                    t_start = time.perf_counter()
-                    while time.perf_counter() - t_start < 0.2:
-                        step()
-                    torch.cuda.synchronize()
-                    # The median of five blocks of `steps` steps: one block that meets a
-                    # clock or power transient does not set the figure.
-                    blocks = []
-                    for _ in range(5):
-                        a = torch.cuda.Event(enable_timing=True)
-                        b = torch.cuda.Event(enable_timing=True)
-                        a.record()
-                        for _ in range(steps):
-                            step()
-                        b.record()
-                        torch.cuda.synchronize()
-                        blocks.append(a.elapsed_time(b) / steps * 1e3)
-                    us = sorted(blocks)[2]
-                    rec[f"{engine}_us"] = round(us, 2)
-                    rec[f"{engine}_stream_gbps"] = round(k * n * bits / 8 / (us * 1e-6) / 1e9, 1)
-                    rec[f"{engine}_rows_per_s"] = round(rows / (us * 1e-6), 1)
+                    total_ms, lin_ms, _, _ = time_steps(torch, tq, copies, xt, suh, svh, steps, warmup, engine,
+                                                        shape)
+                    us = total_ms / steps * 1e3
+                    lin_us = sum(lin_ms) / len(lin_ms) * 1e3
+                    rec[engine] = {
+                        "us_per_step": round(us, 2),
+                        "stream_gbps": round(passes(rows) * ab["stream"] / (us * 1e-6) / 1e9, 1),
+                        "rows_per_s": round(rows / (us * 1e-6), 1),
+                        "linear_us": round(lin_us, 2),
+                        "hbm_frac": round(ab["total"] / (lin_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    }
                 out.append(rec)
                 print(json.dumps(rec), file=sys.stderr, flush=True)
+            del copies
     return out
 
 
-def run_env(torch) -> dict:
+def _versions() -> dict:
+    """hipcc and ROCm versions on this machine (the library was built with the compiler
+    its resource record names)."""
+    v = {}
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
+        v["hipcc"] = "; ".join(l.strip() for l in r.stdout.splitlines()[:2])
+    except (OSError, subprocess.SubprocessError):
+        v["hipcc"] = None
+    try:
+        v["rocm"] = Path("/opt/rocm/.info/version").read_text().strip()
+    except OSError:
+        v["rocm"] = None
+    return v
+
+
+def kernel_resources(names) -> dict:
+    """The compiler's record (registers, LDS, scratch, spills) of the named kernels."""
+    if not RESOURCES_FILE.exists():
+        return {"record": None}
+    rec = json.loads(RESOURCES_FILE.read_text())
+    keep = ("vgprs", "agprs", "sgprs", "lds_bytes", "scratch_bytes_per_lane", "sgpr_spill", "vgpr_spill",
+            "occupancy_waves_per_simd")
+    out = {"compiler": rec.get("compiler"),
+           "all_kernels_scratch_free": all(k.get("scratch_bytes_per_lane", 0) == 0 for k in rec["kernels"].values())}
+    for nm in names:
+        k = rec["kernels"].get("tf_exl3::" + nm)
+        if k is not None:
+            out[nm] = {f: k[f] for f in keep if f in k}
+    return out
+
+
+def run_env(torch, kernels) -> dict:
     """The device and software the numbers come from."""
     props = torch.cuda.get_device_properties(0)
     return {
@@ -376,8 +447,27 @@ def run_env(torch) -> dict:
         "arch": getattr(props, "gcnArchName", ""),
         "compute_units": props.multi_processor_count,
         "torch": torch.__version__,
-        "hip": torch.version.hip,
+        "hip_runtime": torch.version.hip,
+        **_versions(),
+        "kernel_resources": kernel_resources(kernels),
         "seeds": {"workload": WORKLOAD_ID, "rule": "1000 * workload + stream"},
+    }
+
+
+def region(torch, tq, trellis, xt, suh_t, svh_t, rows, steps, warmup, engine) -> dict:
+    t, l, _, _ = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t, steps, warmup, engine)
+    abr = algorithmic_bytes(rows)
+    l_avg = sum(l) / len(l)
+    return {
+        "ms_per_step": round(t / steps, 5),
+        "value": round(abr["stream"] / (t / steps * 1e-3) / 1e9, 2),
+        "rows_per_s": round(rows / (t / steps * 1e-3), 1),
+        "kernel": kernel_name(engine, rows),
+        "linear_ms": round(l_avg, 5),
+        "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
+        "hbm_gbps": round(abr["total"] / (l_avg * 1e-3) / 1e9, 2),
+        "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "valu_frac": round(algorithmic_valu_ops(engine, rows) / (l_avg * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
     }
 
 
@@ -393,11 +483,11 @@ def main() -> int:
                          "prompt path (32-row passes, bit-equal to the v_dot2 linear), or rot_in + the v_dot2 "
                          "linear on the strips layout")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-r16", action="store_true", help="skip the 16-row region")
+    ap.add_argument("--no-r16", action="store_true", help="skip the regions beyond the headline")
+    ap.add_argument("--no-configs", action="store_true", help="skip the test suite's workloads")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 1 GiB copy (counter scale)")
     ap.add_argument("--ingest-counters", metavar="DIR", help="write the traffic record from --pmc runs in DIR")
-    ap.add_argument("--configs", action="store_true",
-                    help="time every workload of the test suite (both engines) and print one JSON line")
+    ap.add_argument("--configs", action="store_true", help="time only the test suite's workloads")
     args = ap.parse_args()
 
     if args.ingest_counters:
@@ -423,64 +513,57 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(torch, tq, dev, args.steps)
         return 0
+    csteps = max(10, args.steps // 2)
     if args.configs:
-        print(json.dumps({"configs": time_configs(torch, tq, max(10, args.steps // 4))}))
+        print(json.dumps({"configs": time_configs(torch, tq, csteps, args.warmup)}))
         return 0
 
     rows = args.rows
-    trellis, xt, suh_t, svh_t, host = make_inputs(torch, dev, 16, copies=2)
+    trellis, xt, suh_t, svh_t, host = make_inputs(torch, dev, 16)
     engine = args.engine
+    n_copies = len(trellis)
     head = [tq.repack_strips(t, BITS, IN_DIM, OUT_DIM) for t in trellis] if engine == "strips" else trellis
     total_ms, lin_ms, wall, y = time_steps(torch, tq, head, xt[:rows].contiguous(), suh_t, svh_t,
                                            args.steps, args.warmup, engine)
-    del head
+    head = None
     ms_per_step = total_ms / args.steps
     lin_avg_ms = sum(lin_ms) / len(lin_ms)
     ab = algorithmic_bytes(rows)
-    stream_gbps = ab["stream"] / (ms_per_step * 1e-3) / 1e9
+    stream_gbps = passes(rows) * ab["stream"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["total"] / (lin_avg_ms * 1e-3) / 1e9
     valu_ops = algorithmic_valu_ops(engine, rows)
     valu_achieved = valu_ops / (lin_avg_ms * 1e-3) / 1e12
     traffic = load_traffic(engine, rows)
 
     extra = {}
+    per_rows = {}
+    kernels = {kernel_name(engine, rows)}
     if not args.no_r16:
-        # Both engines at 1, 2, 4, 8 and 16 rows (the metric's range), and the fused path at 1
-        # and 2, same inputs and protocol (the headline is one of them).
+        # Both engines at 1, 2, 4, 8 and 16 rows (the metric's range), the fused path at 1
+        # and 2, the strips layout at 1 and 16, same inputs and protocol.
         table = {}
-        for eng in ("dot2", "mfma", "fused"):
-            for r in ((1, 2) if eng == "fused" else (1, 2, 4, 8, 16)):
-                t, l, _, _ = time_steps(torch, tq, trellis, xt[:r].contiguous(), suh_t, svh_t, args.steps,
-                                        args.warmup, eng)
-                abr = algorithmic_bytes(r)
-                l_avg = sum(l) / len(l)
-                table[f"{eng}_rows{r}"] = {
-                    "ms_per_step": round(t / args.steps, 5),
-                    "value": round(abr["stream"] / (t / args.steps * 1e-3) / 1e9, 2),
-                    "rows_per_s": round(r / (t / args.steps * 1e-3), 1),
-                    "linear_ms": round(l_avg, 5),
-                    "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
-                    "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                    "valu_frac": round(algorithmic_valu_ops(eng, r) / (l_avg * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-                }
-        # The strips layout (each strip one contiguous stream), same stream repacked.
+        for eng in ("dot2", "mfma"):
+            for r in ROW_COUNTS:
+                table[f"{eng}_rows{r}"] = region(torch, tq, trellis, xt, suh_t, svh_t, r, args.steps, args.warmup,
+                                                 eng)
+                kernels.add(kernel_name(eng, r))
+        for r in (1, 2):
+            table[f"fused_rows{r}"] = region(torch, tq, trellis, xt, suh_t, svh_t, r, args.steps, args.warmup,
+                                             "fused")
+            kernels.add(kernel_name("fused", r))
         strips = [tq.repack_strips(t, BITS, IN_DIM, OUT_DIM) for t in trellis]
         torch.cuda.synchronize()
         for r in (1, 16):
-            t, l, _, _ = time_steps(torch, tq, strips, xt[:r].contiguous(), suh_t, svh_t, args.steps,
-                                    args.warmup, "strips")
-            abr = algorithmic_bytes(r)
-            l_avg = sum(l) / len(l)
-            table[f"strips_rows{r}"] = {
-                "ms_per_step": round(t / args.steps, 5),
-                "value": round(abr["stream"] / (t / args.steps * 1e-3) / 1e9, 2),
-                "rows_per_s": round(r / (t / args.steps * 1e-3), 1),
-                "linear_ms": round(l_avg, 5),
-                "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
-                "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "valu_frac": round(algorithmic_valu_ops("strips", r) / (l_avg * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-            }
+            table[f"strips_rows{r}"] = region(torch, tq, strips, xt, suh_t, svh_t, r, args.steps, args.warmup,
+                                              "strips")
         del strips
+        # The best engine at each row count: the roofline of the metric's whole range.
+        for r in ROW_COUNTS:
+            best = min(("dot2", "mfma"), key=lambda e: table[f"{e}_rows{r}"]["linear_ms"])
+            t = table[f"{best}_rows{r}"]
+            per_rows[str(r)] = {"engine": best, "kernel": "tf_exl3::" + t["kernel"], "kernel_ms": t["linear_ms"],
+                                "achieved_gbps": t["hbm_gbps"], "frac": t["hbm_frac"], "valu_frac": t["valu_frac"],
+                                "ms_per_step": t["ms_per_step"], "rows_per_s": t["rows_per_s"]}
 
         # The prompt path against the decode linear on a 128-row prompt (fewer steps: ~2 ms each).
         import numpy as np
@@ -499,6 +582,10 @@ def main() -> int:
                 "steps": psteps,
             }
         extra["engines"] = table
+    del trellis
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        extra["configs"] = time_configs(torch, tq, csteps, args.warmup)
 
     ceiling = read_ceiling(torch, tq, dev)
     cpu = None if args.no_cpu else cpu_baseline(host, rows)
@@ -522,36 +609,38 @@ def main() -> int:
             "in_dim": IN_DIM, "out_dim": OUT_DIM, "bits": BITS, "rows": rows,
             "waves": tq.linear_plan(BITS, rows, IN_DIM, OUT_DIM)["waves"],
             "engine": engine,
-            "stream_copies": len(trellis),
+            "stream_copies": n_copies,
         },
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
-        # The linear issues more VALU work per byte than the chip supplies at its HBM
-        # rate (the same kernel reading an L2-resident stream takes as many cycles), so
-        # its roofline is the VALU's; the HBM side stands next to it.
+        # The HBM roofline of the dominant kernel: algorithmic bytes per launch over its
+        # average duration (HIP events on its stream) against 8 TB/s. The same launch's
+        # VALU fraction stands beside it (the 1-row decode issues more VALU work per byte
+        # than the chip supplies at its HBM rate, so the VALU is what binds it).
         "roofline": {
-            "bound": "alu",
-            "achieved": round(valu_achieved, 3),
-            "peak": round(VALU_PEAK_TOPS, 3),
-            "unit": "T VALU lane-instr/s",
-            "frac": round(valu_achieved / VALU_PEAK_TOPS, 4),
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel": "tf_exl3::" + kernel_name(engine, rows),
             "kernel_ms": round(lin_avg_ms, 5),
             "kernel_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
-            "ops_per_launch": int(valu_ops),
-            "hbm": {
-                "achieved": round(achieved, 2),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "bytes_per_launch": ab["total"],
-                "read_ceiling": round(ceiling, 2),
-                "frac_of_read_ceiling": round(achieved / ceiling, 4),
+            "bytes_per_launch": ab["total"],
+            "read_ceiling_gbps": round(ceiling, 2),
+            "frac_of_read_ceiling": round(achieved / ceiling, 4),
+            "valu": {
+                "achieved": round(valu_achieved, 3),
+                "peak": round(VALU_PEAK_TOPS, 3),
+                "unit": "T VALU lane-instr/s",
+                "frac": round(valu_achieved / VALU_PEAK_TOPS, 4),
+                "ops_per_launch": int(valu_ops),
             },
+            "per_rows": per_rows,
         },
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
-        "env": run_env(torch),
+        "env": run_env(torch, sorted(kernels)),
         **extra,
     }
     print(json.dumps(out))

@@ -60,18 +60,24 @@ def finish_f32(acc32: np.ndarray, svh_bits: np.ndarray, out_dtype: str) -> np.nd
 
 
 def reference_threads() -> int:
-    """Host cores this process may run on (the threaded reference's default width)."""
+    """Host cores this process may run on (the threaded reference's width), capped by
+    OMP_NUM_THREADS where the environment sets a CPU share."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # platforms without CPU affinity
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
 
 
 def linear_f64(z_bits: np.ndarray, trellis: np.ndarray, bits: int, in_dim: int, out_dim: int,
-               svh_bits: np.ndarray, strips=None, strip_chunk: int = 32, threads: int = 1) -> np.ndarray:
+               svh_bits: np.ndarray, strips=None, strip_chunk: int | None = None, threads: int = 1) -> np.ndarray:
     """y64 [rows][128 * len(strips)] for the given 128-column strips (default: all).
 
-    The strips are taken in chunks of `strip_chunk`; each chunk unpacks its columns'
+    The strips are taken in chunks of `strip_chunk` (default 32, or fewer so that every
+    thread of the pool gets a chunk); each chunk unpacks its columns'
     weights, sums z . W in float64 and finishes its blocks. With threads > 1 the chunks
     are spread over a pool of that many threads (the page's float64 references split
     their work by ranges of columns in the same way). A chunk's arithmetic does not
@@ -84,6 +90,8 @@ def linear_f64(z_bits: np.ndarray, trellis: np.ndarray, bits: int, in_dim: int, 
     strips = np.asarray(strips, dtype=np.int64).reshape(-1)
     out = np.empty((z_bits.shape[0], BLOCK * strips.size), dtype=np.float64)
     svh_bits = np.asarray(svh_bits, dtype=np.uint16)
+    if strip_chunk is None:
+        strip_chunk = max(1, min(32, -(-strips.size // max(1, threads))))
 
     def chunk(i0: int) -> None:
         sel = strips[i0 : i0 + strip_chunk]

@@ -58,3 +58,15 @@ def test_more_than_one_gpu_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_algorithmic_bytes_count_the_stream_once_per_pass():
+    # 64 rows run four passes of 16, each streaming the weights once.
+    s8 = K * N
+    ab = bench.algorithmic_bytes(64, 8, K, N, 4)
+    assert ab["stream"] == s8
+    assert ab["total"] == 4 * s8 + 64 * 2 * K + 64 * 4 * N + 2 * N
+    assert bench.passes(1) == bench.passes(16) == 1 and bench.passes(17) == 2
+    # fp16 outputs (Engram) count two bytes each.
+    assert bench.algorithmic_bytes(2, 3, 6144, 25600, 2)["total"] == 6144 * 25600 * 3 // 8 + 2 * 2 * 6144 \
+        + 2 * 2 * 25600 + 2 * 25600

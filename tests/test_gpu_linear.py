@@ -5,7 +5,7 @@ ragged row counts across passes, both wave counts, all widths, three output
 types), the page's identity test (outputs are weight rows through the fp32
 output rotation, bit for bit), its exactness gate (all-ones states, k = 6144,
 inputs 4096: bit for bit), batch invariance across windows and passes,
-five-run byte identity, non-finite classes, and the two planted controls
+five-run byte identity (batch invariance is in test_gpu_windows.py), non-finite classes, and the two planted controls
 (inputs one row late, the wrong width) launched on the real kernel.
 """
 
@@ -88,29 +88,6 @@ def test_exact_gate(gpu, engine, bits, waves):
     want = lin.finish_f32(acc, svh, "f32")[0]
     assert same_bits(y, want)
     assert abs(int(nf.f32_bits(y[0])) & 0x7FFFFFFF) == 0x4D31CB0C
-
-
-@ENGINES
-@pytest.mark.parametrize("bits", tr.WIDTHS)
-def test_batch_invariance(gpu, engine, bits):
-    """Each row's bits alone, in windows of 2..24 rows from several first rows, and in
-    one 64-row launch (four passes of 16), at 8 waves on 6144 -> 25600."""
-    k, n, rows = 6144, 25600, 64
-    stream, z, svh = make(bits, k, n, rows, 700 + bits)
-    say(f"batch invariance {engine} bits={bits}")
-    tt = up(stream)
-    full = linear(z, None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
-    for r in range(rows):
-        alone = linear(z[r : r + 1], None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
-        assert np.array_equal(nf.f32_bits(alone[0]), nf.f32_bits(full[r])), r
-    for size in range(2, 25):
-        for first in sorted({0, 5, 16 - size // 2, rows - size}):
-            if first < 0 or first + size > rows:
-                continue
-            win = linear(z[first : first + size], None, svh, bits, n, "f32", 8, stream_t=tt, engine=engine)
-            assert np.array_equal(nf.f32_bits(win), nf.f32_bits(full[first : first + size])), (size, first)
-    y64 = lin.linear_f64(z, stream, bits, k, n, svh, strips=[0, 77, 199])
-    assert lin.gate_error(full[:, lin.strip_columns([0, 77, 199])], "f32", y64) <= lin.GATE
 
 
 @ENGINES

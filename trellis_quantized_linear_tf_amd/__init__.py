@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     calib_stream_read,
     debug_decode_tiles,
     debug_linear_split,
+    debug_linear_mfma_split,
     header_functions,
     linear,
     linear_plan,

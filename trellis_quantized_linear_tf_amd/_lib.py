@@ -57,6 +57,7 @@ SIGNATURES = {
     "tf_exl3_linear_strips": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_repack_strips": (_I, [_I, _I, _I, _P, _P, _P]),
     "tf_exl3_debug_linear_split": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "tf_exl3_debug_linear_mfma_split": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
     "tf_exl3_project": (_I, [_I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "tf_exl3_project_pass_rows": (_I, [_I, _I, _I, _I]),
     "tf_exl3_linear_plan": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
@@ -330,6 +331,19 @@ def debug_linear_split(z, trellis, svh, bits: int, out_dim: int, split: int, y=N
         y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
     _check(load().tf_exl3_debug_linear_split(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh), _ptr(y),
                                              _dt_code(y.dtype), waves, split, _stream(z)))
+    return y
+
+
+def debug_linear_mfma_split(z, trellis, svh, bits: int, out_dim: int, split: int, y=None, out_dtype=None,
+                            waves: int = 0):
+    """tf_exl3_linear_mfma with its form forced: split 0 (one workgroup's waves per strip)
+    or split 1 (the column-split form, 4 waves only) (tf_exl3_debug_linear_mfma_split)."""
+    torch = _torch()
+    rows, in_dim = _check_linear_args(z, trellis, svh, bits, out_dim, y, out_dtype)
+    if y is None:
+        y = torch.empty((rows, out_dim), dtype=out_dtype or torch.float32, device=z.device)
+    _check(load().tf_exl3_debug_linear_mfma_split(bits, rows, in_dim, out_dim, _ptr(z), _ptr(trellis), _ptr(svh),
+                                                  _ptr(y), _dt_code(y.dtype), waves, split, _stream(z)))
     return y
 
 

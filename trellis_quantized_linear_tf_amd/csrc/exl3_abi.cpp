@@ -169,6 +169,20 @@ int tf_exl3_debug_linear_split(int bits, int rows, int in_dim, int out_dim, cons
   return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
 }
 
+int tf_exl3_debug_linear_mfma_split(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
+                                    const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype, int waves,
+                                    int split, void* stream) {
+  if (split != 0 && split != 1) return TF_E_SHAPE;
+  tf_exl3_plan plan;
+  const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
+  if (st != TF_OK) return st;
+  if (split == 1 && plan.waves != 4) return TF_E_SHAPE;
+  if (rows == 0) return TF_OK;
+  const hipError_t e = tf_exl3::launch_linear_mfma(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
+                                                   y_dtype, static_cast<hipStream_t>(stream), split);
+  return e == hipSuccess ? TF_OK : TF_E_LAUNCH;
+}
+
 int tf_exl3_linear_strips(int bits, int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* strips,
                           const uint16_t* svh, void* y, int y_dtype, int waves, void* stream) {
   tf_exl3_plan plan;
