@@ -256,9 +256,9 @@ int tf_exl3_debug_linear_split(int bits, int rows, int in_dim, int out_dim, cons
 int tf_exl3_debug_decode_tiles(int bits, int in_dim, int out_dim, const uint32_t* trellis,
                                uint16_t* w, void* stream);
 /* debug_linear_mfma_split: tf_exl3_linear_mfma with its form forced at 4 waves (split 0:
- * every strip on one workgroup's waves, 1: the column-split form); at 8 waves split must
- * be 0. Both forms give the same bits, which the tests check; split outside {0, 1}, or 1
- * at 8 waves, is TF_E_SHAPE. */
+ * each strip's 8 column tiles on every wave, 1: in halves over twice the waves); at 8 waves
+ * split must be 0. Both forms give the same bits, which the tests check; split outside
+ * {0, 1}, or 1 at 8 waves, is TF_E_SHAPE. */
 int tf_exl3_debug_linear_mfma_split(int bits, int rows, int in_dim, int out_dim, const uint16_t* z,
                                     const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                                     int waves, int split, void* stream);

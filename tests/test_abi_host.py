@@ -148,15 +148,16 @@ def test_rot_in_refusals(lib):
 
 
 def test_debug_split_refusals(lib):
-    for f in (lib.tf_exl3_debug_linear_split, lib.tf_exl3_debug_linear_mfma_split):
+    for f, top in ((lib.tf_exl3_debug_linear_split, 1), (lib.tf_exl3_debug_linear_mfma_split, 1)):
         args = [4, 2, 256, 256, FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, 0, 4]
-        assert f(*args, 2, None) == -2  # split outside {0, 1}
+        assert f(*args, top + 1, None) == -2  # split outside the forms
         assert f(*args, -1, None) == -2
         assert f(4, 2, 256, 200, *args[4:], 0, None) == -2
         assert f(*args[:4], None, *args[5:], 0, None) == -5
     # The matrix-core column split exists at 4 waves only.
-    assert lib.tf_exl3_debug_linear_mfma_split(4, 2, 256, 256, FAKE, FAKE + 0x100000, FAKE + 0x200000,
-                                               FAKE + 0x300000, 0, 8, 1, None) == -2
+    for split in (1,):
+        assert lib.tf_exl3_debug_linear_mfma_split(4, 2, 256, 256, FAKE, FAKE + 0x100000, FAKE + 0x200000,
+                                                   FAKE + 0x300000, 0, 8, split, None) == -2
 
 
 def test_debug_refusals(lib):

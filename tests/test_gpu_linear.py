@@ -177,3 +177,20 @@ def test_mfma_column_split_same_bits(gpu, bits, k, rows):
     assert same_bits(yn, yw[:, :n_narrow])
     y64 = lin.linear_f64(z, narrow, bits, k, n_narrow, svh[:n_narrow])
     assert lin.gate_error(yn, "f32", y64) <= lin.GATE
+
+
+@pytest.mark.parametrize("bits", tr.WIDTHS)
+@pytest.mark.parametrize("k,n,rows", [(384, 1024, 3), (640, 256, 17), (6144, 1280, 16)])
+def test_mfma_forms_same_bits(gpu, bits, k, n, rows):
+    """The matrix-core linear's two forms at 4 waves (each strip's 8 column tiles on
+    every wave, or in halves over twice the waves) run the same MFMAs per column in
+    the same order: bit-identical outputs, within the gate."""
+    stream, z, svh = make(bits, k, n, rows, 930 + bits + k)
+    say(f"mfma forms bits={bits} k={k} n={n} rows={rows}")
+    zt, tt, vt = up(z), up(stream), up(svh)
+    ys = [down(tq.debug_linear_mfma_split(zt, tt, vt, bits, n, split, waves=4)) for split in (0, 1)]
+    torch.cuda.synchronize()
+    assert same_bits(ys[1], ys[0])
+    assert same_bits(linear(z, None, svh, bits, n, "f32", 4, stream_t=tt, engine="mfma"), ys[1])
+    y64 = lin.linear_f64(z, stream, bits, k, n, svh)
+    assert lin.gate_error(ys[1], "f32", y64) <= lin.GATE

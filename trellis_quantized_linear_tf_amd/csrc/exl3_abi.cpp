@@ -176,7 +176,7 @@ int tf_exl3_debug_linear_mfma_split(int bits, int rows, int in_dim, int out_dim,
   tf_exl3_plan plan;
   const int st = linear_checks(bits, rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, waves, &plan);
   if (st != TF_OK) return st;
-  if (split == 1 && plan.waves != 4) return TF_E_SHAPE;
+  if (split != 0 && plan.waves != 4) return TF_E_SHAPE;
   if (rows == 0) return TF_OK;
   const hipError_t e = tf_exl3::launch_linear_mfma(bits, plan.waves, rows, in_dim, out_dim, z, trellis, svh, y,
                                                    y_dtype, static_cast<hipStream_t>(stream), split);

@@ -91,15 +91,16 @@ hipError_t launch_linear_prompt(int bits, int waves, int rows, int in_dim, int o
                                 const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                                 hipStream_t stream);
 
-// The matrix-core linear at 4 waves runs its column-split form (twice the waves,
-// the same bits) where the first form would put fewer waves than SIMDs in flight.
+// The matrix-core linear at 4 waves runs its column-split form (each strip's
+// columns in two halves over twice the waves, the same bits) where the first form
+// would put fewer waves than SIMDs in flight.
 constexpr long long kMfmaSplitBelowWaves = 1024;
 
-inline bool mfma_column_split(int bits, int out_dim, int waves) {
-  return waves == 4 && (long long)(out_dim / 128) * waves < kMfmaSplitBelowWaves;
+inline int mfma_column_parts(int out_dim, int waves) {
+  return waves == 4 && (long long)(out_dim / 128) * waves < kMfmaSplitBelowWaves ? 2 : 1;
 }
 
-// split: -1 = by mfma_column_split(), 0 = never, 1 = always at 4 waves.
+// split: -1 = by mfma_column_parts(), 0 = the first form, 1 = halves (4 waves only).
 hipError_t launch_linear_mfma(int bits, int waves, int rows, int in_dim, int out_dim, const uint16_t* z,
                               const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                               hipStream_t stream, int split = -1);

@@ -31,7 +31,12 @@ __global__ __launch_bounds__(kWave * 2 * WAVES) void linear_cs_kernel(const uint
                                                                       const uint16_t* __restrict__ svh,
                                                                       void* __restrict__ y, int y_dtype, int rows,
                                                                       int in_dim, int out_dim, int layout) {
-  constexpr int PF = prefetch_depth<BITS>();
+  // Twice the regular kernel's tile rows in flight: a narrow launch has about two
+  // waves per SIMD, so each wave must carry twice the stream bytes in flight for the
+  // device to hold as many as the latency of HBM asks for (vector registers are
+  // plentiful at this occupancy). Passes of 2 and 4 rows keep the regular depth:
+  // their scalar z loads for the longer unrolled ring would not fit the SGPRs.
+  constexpr int PF = (NR == 1 || NR > kScalarZRows ? 2 : 1) * prefetch_depth<BITS>();
   constexpr int RING = PF + 1;
   constexpr int CW = column_words<BITS>();
   constexpr int ND = BITS % 2 ? CW + 1 : CW;  // dwords loaded per lane

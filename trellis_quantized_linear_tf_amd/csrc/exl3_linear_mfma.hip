@@ -29,7 +29,7 @@
 // row's bits never depend on the rows that share its launch. The order is a
 // different fixed one from the v_dot2 linear's: the two agree to the float64
 // gate, not bit for bit. Narrow matrices at 4 waves run a column-split form
-// with the same bits (see linear_mfma_kernel's HALVES).
+// with the same bits (see linear_mfma_kernel's PARTS).
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
@@ -95,47 +95,62 @@ __device__ __forceinline__ void khalf_states(const uint32_t (&a)[khalf_words<BIT
 }
 
 // LDS stage of one pair's stream for one wave: two tile rows of the wave's
-// tiles (all 8, or 4 in the column-split form), the second padded to start 32
-// banks (mod 64) after the first, so the two halves of the wave, which read
-// different tile rows, read different banks.
-template <int BITS, int HALVES>
+// tiles (all 8, or 8 / PARTS in the column-split forms), the second padded to
+// start 32 banks (mod 64) after the first, so the two halves of the wave, which
+// read different tile rows, read different banks.
+template <int BITS, int PARTS>
 constexpr int stage_row_words() {
-  return 64 * BITS / HALVES + (96 - (64 * BITS / HALVES) % 64) % 64;
+  return 64 * BITS / PARTS + (96 - (64 * BITS / PARTS) % 64) % 64;
 }
-template <int BITS, int HALVES>
+template <int BITS, int PARTS>
 constexpr int stage_words() {
-  return 2 * stage_row_words<BITS, HALVES>();
+  return 2 * stage_row_words<BITS, PARTS>();
+}
+
+// Lanes that load a tile row of the wave's tiles (WORDS dwords): 64, or 32 where
+// 64 does not divide it (the split form at odd widths); lanes past them repeat
+// their words (the same line, coalesced) and write the same values to the same
+// stage words.
+template <int WORDS>
+constexpr int load_lanes() {
+  return WORDS % 64 == 0 ? 64 : 32;
 }
 constexpr int kWaveLdsWords = kRowsPerPass * kBlock;  // one k-wave's partial sums, 8 KiB
 
-// HALVES = 1: WAVES waves, each decodes all 8 tiles of its pairs; its stage
-// lives in its own partial-sum area. HALVES = 2 (column split, for launches with
-// fewer waves than SIMDs): 2 * WAVES waves, wave (h, w) takes the same pairs as
-// wave w of the first form but only tiles 4h .. 4h + 3 (strip columns 64h ..
-// 64h + 63), so each column sees the same MFMAs in the same order and the same
-// cross-wave sum: the outputs are bit-identical to the first form's.
-template <int BITS, int WAVES, int HALVES>
-__global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
+// PARTS = 1: WAVES waves, each decodes all 8 tiles of its pairs; its stage
+// lives in its own partial-sum area. PARTS = 2 (column split, for narrow
+// launches): 2 * WAVES waves, wave (h, w) takes the same pairs as wave w of the
+// first form but only tiles 4h .. 4h + 3 (NT = 8 / PARTS), so each column sees
+// the same MFMAs in the same order and the same cross-wave sum: the outputs are
+// bit-identical to the first form's. (Quarters over four times the waves were
+// measured too: no faster at one row, slower at 16, where every extra wave
+// loads its own A operand.)
+template <int BITS, int WAVES, int PARTS>
+__global__ __launch_bounds__(kWave* WAVES* PARTS) __attribute__((amdgpu_waves_per_eu(4))) void linear_mfma_kernel(
     const uint16_t* __restrict__ z, const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh,
     void* __restrict__ y, int y_dtype, int rows, int in_dim, int out_dim) {
   constexpr int NR = kRowsPerPass;
-  constexpr int NT = 8 / HALVES;  // tiles (MFMAs) per wave and pair
+  constexpr int NT = 8 / PARTS;  // tiles (MFMAs) per wave and pair
   constexpr int CW = khalf_raw_words<BITS>();
   constexpr int KW = khalf_words<BITS>();
   // Pairs in flight. The stage takes step i + 1's stream during step i, so PF
   // pairs in flight give PF - 1 steps of cover: at least 2, except the 8-bit
   // first form, where a second pair spills past 128 VGPRs (measured on the 8-bit
   // LM head at 16 rows: 145 us against 140 with one pair; its many waves cover).
-  constexpr int PF = BITS == 8 && HALVES == 1 ? 1 : prefetch_depth<BITS>() / 2 > 2 ? prefetch_depth<BITS>() / 2 : 2;
+  // The column-split form runs narrow launches at about two waves per SIMD, so
+  // each wave keeps twice the pairs in flight (a pair is half the first form's
+  // bytes there).
+  constexpr int PF_WIDE = prefetch_depth<BITS>() / 2 > 2 ? prefetch_depth<BITS>() / 2 : 2;
+  constexpr int PF = PARTS >= 2 ? 2 * PF_WIDE : BITS == 8 ? 1 : PF_WIDE;
   constexpr int RING = PF + 1;
-  constexpr int RS = stage_row_words<BITS, HALVES>();  // stage words from tile row 2p to 2p + 1
+  constexpr int RS = stage_row_words<BITS, PARTS>();  // stage words from tile row 2p to 2p + 1
   // Loads of a tile row's NT tiles (8 * BITS * NT words): LW lanes take PW contiguous dwords each.
-  constexpr int LW = HALVES == 1 || BITS % 2 == 0 ? kWave : kWave / 2;
+  constexpr int LW = load_lanes<8 * BITS * NT>();
   constexpr int PW = 8 * BITS * NT / LW;
   static_assert(LW * PW == 8 * BITS * NT, "the wave's loads cover its tiles");
-  static_assert(HALVES == 1 ? stage_words<BITS, 1>() <= kWaveLdsWords : true, "the stage fits the partial area");
-  constexpr int LDS_WORDS = HALVES == 1 ? WAVES * kWaveLdsWords
-                                        : WAVES * kWaveLdsWords + WAVES * HALVES * stage_words<BITS, HALVES>();
+  static_assert(PARTS == 1 ? stage_words<BITS, 1>() <= kWaveLdsWords : true, "the stage fits the partial area");
+  constexpr int LDS_WORDS = PARTS == 1 ? WAVES * kWaveLdsWords
+                                       : WAVES * kWaveLdsWords + WAVES * PARTS * stage_words<BITS, PARTS>();
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_WORDS];
 
   const int lane = __lane_id();
@@ -147,12 +162,13 @@ __global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_p
   const int nr = min(NR, rows - r0);
   const int pairs = in_dim / 32;
   const int iters = (pairs - wave + WAVES - 1) / WAVES;  // 0 when in_dim = 128 and WAVES = 8, wave >= 4
-  uint32_t* const stage = HALVES == 1 ? lds + wave * kWaveLdsWords
-                                      : lds + WAVES * kWaveLdsWords + hw * stage_words<BITS, HALVES>();
+  uint32_t* const stage = PARTS == 1 ? lds + wave * kWaveLdsWords
+                                     : lds + WAVES * kWaveLdsWords + hw * stage_words<BITS, PARTS>();
 
   // Stream walk: tile rows 2p and 2p + 1 of the wave's pair p, its NT tiles of
-  // each (one coalesced load per tile row; in the split form at odd widths half
-  // the lanes repeat the other half's words, which they write to the same place).
+  // each (one coalesced load per tile row; in the split forms, where a tile row of
+  // NT tiles is fewer than 64 lanes' dwords, lanes past LW repeat a lower lane's
+  // words, which they write to the same place).
   const StreamStrides st = stream_strides<BITS>(kLayoutTiles, in_dim, out_dim);
   const uint32_t* __restrict__ tbase = trellis + (size_t)strip * st.strip + half * NT * 8 * BITS;
   const int off = (lane % LW) * PW;
@@ -203,11 +219,11 @@ __global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_p
   auto step = [&](auto dc, int i) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     issue(ring[(D + PF) % RING], zr[(D + PF) % RING], i + PF);
-    // In the split form (registers to spare) this keeps the loads at the top of
+    // In the split forms (registers to spare) this keeps the loads at the top of
     // the step: left to itself the scheduler sank them below the decode at 3
     // bits, and the next step's stage write then waited for loads just issued.
     // The first form keeps the scheduler's order: there the pin costs spills.
-    if constexpr (HALVES == 2) asm volatile("" ::: "memory");
+    if constexpr (PARTS >= 2) asm volatile("" ::: "memory");
     uint32_t kh[NT][CW];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
@@ -250,28 +266,28 @@ __global__ __launch_bounds__(kWave* WAVES* HALVES) __attribute__((amdgpu_waves_p
     }
   }
   __syncthreads();
-  finish_strip<WAVES, WAVES * HALVES>(partial, NR, hw, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
+  finish_strip<WAVES, WAVES * PARTS>(partial, NR, hw, lane, nr, r0, strip, out_dim, svh, y, y_dtype);
 }
 
-template <int BITS, int WAVES, int HALVES>
+template <int BITS, int WAVES, int PARTS>
 static hipError_t launch_mfma_bwh(int rows, int in_dim, int out_dim, const uint16_t* z, const uint32_t* trellis,
                                   const uint16_t* svh, void* y, int y_dtype, hipStream_t stream) {
   const dim3 grid(out_dim / kBlock, (rows + kRowsPerPass - 1) / kRowsPerPass);
-  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES, HALVES>), grid, dim3(kWave * WAVES * HALVES), 0, stream, z,
+  hipLaunchKernelGGL((linear_mfma_kernel<BITS, WAVES, PARTS>), grid, dim3(kWave * WAVES * PARTS), 0, stream, z,
                      trellis, svh, y, y_dtype, rows, in_dim, out_dim);
   return hipGetLastError();
 }
 
-// The column-split form runs where the first form would put fewer waves than
+// The column-split forms run where the first form would put fewer waves than
 // the device has SIMDs (1024 on MI355X) in flight, at 4 waves (see
-// mfma_column_split); the choice depends on the shape and width, never on the rows.
+// mfma_column_parts); the choice depends on the shape, never on the rows.
 template <int BITS>
 static hipError_t launch_mfma_b(int waves, int split, int rows, int in_dim, int out_dim, const uint16_t* z,
                                 const uint32_t* trellis, const uint16_t* svh, void* y, int y_dtype,
                                 hipStream_t stream) {
   if (waves == 8) return launch_mfma_bwh<BITS, 8, 1>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
-  const bool halves = split < 0 ? mfma_column_split(BITS, out_dim, waves) : split == 1;
-  if (halves) return launch_mfma_bwh<BITS, 4, 2>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
+  const int parts = split < 0 ? mfma_column_parts(out_dim, waves) : split == 0 ? 1 : 2;
+  if (parts == 2) return launch_mfma_bwh<BITS, 4, 2>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
   return launch_mfma_bwh<BITS, 4, 1>(rows, in_dim, out_dim, z, trellis, svh, y, y_dtype, stream);
 }
 

@@ -18,13 +18,21 @@
 
 namespace tf_exl3 {
 
+// Waves per SIMD the single launch is compiled for: at one row a pass, 8, so that a
+// grid as wide as the LM head's (1010 workgroups of 8 waves) is resident at once (at
+// 6 waves per SIMD three quarters of it were, and the rest ran as a second
+// generation behind them); larger passes keep the compiler's choice (at 2 rows and
+// 6 bits the 64-register budget of 8 waves would spill).
+template <int NR>
+constexpr int project_waves_per_eu() {
+  return NR == 1 ? 8 : 1;
+}
+
 template <int BITS, int WAVES, int NR>
-__global__ __launch_bounds__(kWave* WAVES) void project_kernel(const void* __restrict__ x, int x_dtype,
-                                                               const uint16_t* __restrict__ suh,
-                                                               const uint32_t* __restrict__ trellis,
-                                                               const uint16_t* __restrict__ svh,
-                                                               void* __restrict__ y, int y_dtype, int rows,
-                                                               int in_dim, int out_dim) {
+__global__ __launch_bounds__(kWave* WAVES) __attribute__((amdgpu_waves_per_eu(project_waves_per_eu<NR>()))) void
+project_kernel(const void* __restrict__ x, int x_dtype, const uint16_t* __restrict__ suh,
+               const uint32_t* __restrict__ trellis, const uint16_t* __restrict__ svh, void* __restrict__ y,
+               int y_dtype, int rows, int in_dim, int out_dim) {
   extern __shared__ uint32_t lds[];  // z: [NR][in_dim] fp16, then partial: [WAVES][NR][128] fp32
   uint16_t* zl = reinterpret_cast<uint16_t*>(lds);
   float* partial = reinterpret_cast<float*>(lds + (size_t)NR * in_dim / 2);
@@ -43,8 +51,9 @@ __global__ __launch_bounds__(kWave* WAVES) void project_kernel(const void* __res
   // rot_in of this pass's rows into LDS: wave w takes 128-blocks w, w + WAVES, ...
   // in chunks of kChunk. A chunk's loads all go out before its first use, and the
   // first chunk's before the stream prime (loads complete in issue order, so the
-  // rotation never waits behind the stream).
-  constexpr int kChunk = 8;
+  // rotation never waits behind the stream). Four blocks a chunk keep the registers
+  // of the loads in flight within the 8-waves-per-SIMD budget.
+  constexpr int kChunk = 4;
   const int bpr = in_dim / kBlock;
   const int total = nr * bpr;
   bool primed = false;
