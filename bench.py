@@ -171,12 +171,17 @@ class Shape:
 
 def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, engine: str = "dot2",
                shape: Shape | None = None):
-    """Warm up, then two timed regions of exactly `steps` steps each: the steps alone
-    (events only before and after: ms per step), then the same steps with HIP events
-    around every launch of the linear's kernel, on the stream it is launched on (its
-    duration: the events themselves cost the step a few microseconds, so they stay out
-    of the first region). Step i reads stream copy (warmup + i) mod copies, so the
-    timed steps start on the copies written longest ago."""
+    """Warm up, then three timed regions of exactly `steps` steps each, on the stream the
+    kernels are launched on:
+      1. the steps alone, one event pair around the region: ms per step;
+      2. the linear's launches alone, back to back on the same z (rot_in ran once before),
+         one event pair around the region: the kernel's average launch duration (it
+         includes the short gap between back-to-back kernels, not a dispatch latency);
+      3. the steps with an event pair around every linear launch: the spread (p10, p50,
+         p90) of single launches, whose pairs also span the dispatch latency.
+    Step i reads stream copy (warmup + i) mod copies, so the timed steps start on the
+    copies written longest ago. Returns (region-1 ms, region-2 ms per launch, region-3
+    per-launch ms list, wall seconds of region 1, y)."""
     sh = shape or Shape()
     rows = xt.shape[0]
     z = torch.empty((rows, sh.k), dtype=torch.float16, device=xt.device)
@@ -219,12 +224,29 @@ def time_steps(torch, tq, trellis, xt, suh_t, svh_t, steps: int, warmup: int, en
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
 
+    def launch(i):
+        t = trellis[i % copies]
+        if engine == "fused":
+            tq.project(xt, suh_t, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves)
+        else:
+            tq.linear(z, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves, engine=engine)
+
+    if engine != "fused":
+        tq.rot_in(xt, suh_t, z)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for j in range(steps):
+        launch(base + steps + j)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = t0.elapsed_time(t1) / steps
+
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for j in range(steps):
-        step(base + steps + j, ev[j])
+        step(base + 2 * steps + j, ev[j])
     torch.cuda.synchronize()
     lin_ms = [a.elapsed_time(b) for a, b in ev]
-    return total_ms, lin_ms, wall, y
+    return total_ms, kernel_ms, lin_ms, wall, y
 
 
 def _percentiles(v):
@@ -390,10 +412,10 @@ def time_configs(torch, tq, steps: int, warmup: int) -> list:
                        "waves": tq.linear_plan(bits, rows, k, n, waves)["waves"], "stream_copies": len(copies),
                        "bytes_per_launch": ab["total"]}
                 for engine in ("dot2", "mfma"):
-                    total_ms, lin_ms, _, _ = time_steps(torch, tq, copies, xt, suh, svh, steps, warmup, engine,
-                                                        shape)
+                    total_ms, kernel_ms, _, _, _ = time_steps(torch, tq, copies, xt, suh, svh, steps, warmup,
+                                                              engine, shape)
                     us = total_ms / steps * 1e3
-                    lin_us = sum(lin_ms) / len(lin_ms) * 1e3
+                    lin_us = kernel_ms * 1e3
                     rec[engine] = {
                         "us_per_step": round(us, 2),
                         "stream_gbps": round(passes(rows) * ab["stream"] / (us * 1e-6) / 1e9, 1),
@@ -455,16 +477,15 @@ def run_env(torch, kernels) -> dict:
 
 
 def region(torch, tq, trellis, xt, suh_t, svh_t, rows, steps, warmup, engine) -> dict:
-    t, l, _, _ = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t, steps, warmup, engine)
+    t, l_avg, l, _, _ = time_steps(torch, tq, trellis, xt[:rows].contiguous(), suh_t, svh_t, steps, warmup, engine)
     abr = algorithmic_bytes(rows)
-    l_avg = sum(l) / len(l)
     return {
         "ms_per_step": round(t / steps, 5),
         "value": round(abr["stream"] / (t / steps * 1e-3) / 1e9, 2),
         "rows_per_s": round(rows / (t / steps * 1e-3), 1),
         "kernel": kernel_name(engine, rows),
         "linear_ms": round(l_avg, 5),
-        "linear_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
+        "single_launch_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(l)],
         "hbm_gbps": round(abr["total"] / (l_avg * 1e-3) / 1e9, 2),
         "hbm_frac": round(abr["total"] / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "valu_frac": round(algorithmic_valu_ops(engine, rows) / (l_avg * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
@@ -523,11 +544,10 @@ def main() -> int:
     engine = args.engine
     n_copies = len(trellis)
     head = [tq.repack_strips(t, BITS, IN_DIM, OUT_DIM) for t in trellis] if engine == "strips" else trellis
-    total_ms, lin_ms, wall, y = time_steps(torch, tq, head, xt[:rows].contiguous(), suh_t, svh_t,
-                                           args.steps, args.warmup, engine)
+    total_ms, lin_avg_ms, lin_ms, wall, y = time_steps(torch, tq, head, xt[:rows].contiguous(), suh_t, svh_t,
+                                                       args.steps, args.warmup, engine)
     head = None
     ms_per_step = total_ms / args.steps
-    lin_avg_ms = sum(lin_ms) / len(lin_ms)
     ab = algorithmic_bytes(rows)
     stream_gbps = passes(rows) * ab["stream"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["total"] / (lin_avg_ms * 1e-3) / 1e9
@@ -574,11 +594,11 @@ def main() -> int:
         xpt = torch.from_numpy(xp.view(np.int16)).to(dev).view(torch.float16)
         psteps = max(10, args.steps // 10)
         for eng in ("dot2", "prompt"):
-            t, l, _, _ = time_steps(torch, tq, trellis, xpt, suh_t, svh_t, psteps, args.warmup, eng)
+            t, l_avg, _, _, _ = time_steps(torch, tq, trellis, xpt, suh_t, svh_t, psteps, args.warmup, eng)
             table[f"{eng}_rows{PROMPT_ROWS}"] = {
                 "ms_per_step": round(t / psteps, 5),
                 "rows_per_s": round(PROMPT_ROWS / (t / psteps * 1e-3), 1),
-                "linear_ms": round(sum(l) / len(l), 5),
+                "linear_ms": round(l_avg, 5),
                 "steps": psteps,
             }
         extra["engines"] = table
@@ -625,7 +645,8 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "tf_exl3::" + kernel_name(engine, rows),
             "kernel_ms": round(lin_avg_ms, 5),
-            "kernel_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
+            "kernel_ms_timing": "events around the region of back-to-back launches of the kernel",
+            "single_launch_ms_p10_p50_p90": [round(v, 5) for v in _percentiles(lin_ms)],
             "bytes_per_launch": ab["total"],
             "read_ceiling_gbps": round(ceiling, 2),
             "frac_of_read_ceiling": round(achieved / ceiling, 4),
