@@ -384,9 +384,12 @@ _TDT = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 def time_configs(torch, tq, steps: int, warmup: int) -> list:
-    """Every workload on both engines under the bench's protocol (rotating stream copies
-    over 1.2 GB, warm-up, ms per step from a region without per-launch events, the
-    linear's kernel time from events around each launch)."""
+    """Every workload on both engines, and through the single launch where one pass holds
+    its rows, under the bench's protocol (rotating stream copies over 1.2 GB, warm-up, us
+    per step from a region of whole steps, the kernel's time from a region of its
+    launches back to back; for the single launch that kernel is the whole step). Each
+    also reports the step replayed from HIP graphs (time_graph_steps), which removes the
+    per-launch overhead that dominates the latency-bound shapes."""
     import numpy as np
 
     import synth
@@ -411,13 +414,17 @@ def time_configs(torch, tq, steps: int, warmup: int) -> list:
                 rec = {"workload": name, "bits": bits, "rows": rows, "x": xdt, "y": ydt,
                        "waves": tq.linear_plan(bits, rows, k, n, waves)["waves"], "stream_copies": len(copies),
                        "bytes_per_launch": ab["total"]}
-                for engine in ("dot2", "mfma"):
+                # The single launch (rot_in fused into the v_dot2 linear) where one launch
+                # holds all the rows: it saves a launch, which matters on latency-bound shapes.
+                fused = rows <= tq.project_pass_rows(rows, k, n, waves)
+                for engine in ("dot2", "mfma") + (("fused",) if fused else ()):
                     total_ms, kernel_ms, _, _, _ = time_steps(torch, tq, copies, xt, suh, svh, steps, warmup,
                                                               engine, shape)
                     us = total_ms / steps * 1e3
                     lin_us = kernel_ms * 1e3
                     rec[engine] = {
                         "us_per_step": round(us, 2),
+                        "graph_us_per_step": round(time_graph_steps(torch, tq, copies, xt, suh, svh, engine, shape), 2),
                         "stream_gbps": round(passes(rows) * ab["stream"] / (us * 1e-6) / 1e9, 1),
                         "rows_per_s": round(rows / (us * 1e-6), 1),
                         "linear_us": round(lin_us, 2),
@@ -427,6 +434,55 @@ def time_configs(torch, tq, steps: int, warmup: int) -> list:
                 print(json.dumps(rec), file=sys.stderr, flush=True)
             del copies
     return out
+
+
+GRAPH_STEPS = 32  # steps per captured graph (each on its own stream copy)
+
+
+def time_graph_steps(torch, tq, trellis, xt, suh_t, svh_t, engine: str, shape: Shape, replays: int = 20) -> float:
+    """us per step when a caller replays its steps as HIP graphs: four graphs of
+    GRAPH_STEPS steps each (rot_in + linear, or the single launch), step i of graph j on
+    stream copy (j * GRAPH_STEPS + i) mod copies, captured once and replayed in turn; one
+    event pair around `replays` replays."""
+    sh = shape
+    rows = xt.shape[0]
+    z = torch.empty((rows, sh.k), dtype=torch.float16, device=xt.device)
+    y = torch.empty((rows, sh.n), dtype=sh.y_dtype or torch.float32, device=xt.device)
+    copies = len(trellis)
+
+    def step(t):
+        if engine == "fused":
+            tq.project(xt, suh_t, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves)
+        else:
+            tq.rot_in(xt, suh_t, z)
+            tq.linear(z, t, svh_t, sh.bits, sh.n, y=y, waves=sh.waves, engine=engine)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(trellis[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for j in range(4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(GRAPH_STEPS):
+                step(trellis[(j * GRAPH_STEPS + i) % copies])
+        graphs.append(g)
+    for r in range(8):
+        graphs[r % 4].replay()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for r in range(replays):
+        graphs[r % 4].replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / (replays * GRAPH_STEPS) * 1e3
+    del graphs
+    return us
 
 
 def _versions() -> dict:
