@@ -266,8 +266,10 @@ def cpu_baseline(host_inputs, rows: int) -> dict:
     stream, x, suh, svh = host_inputs
     threads = lin.reference_threads()
     n_strips = OUT_DIM // 128
-    sample = n_strips if threads >= 8 else 384  # about 10-30 s of CPU work either way
-    strips = np.arange(sample)
+    # A bounded sample: 32 strips per thread (about 0.11 s of CPU work per strip, so
+    # about 30 s of CPU work on 16 threads), spread evenly over the head's strips.
+    sample = min(n_strips, 32 * threads)
+    strips = np.linspace(0, n_strips - 1, sample).round().astype(np.int64)
     z = rot.rot_in(x[:rows], "f16", suh)
     t0 = time.perf_counter()
     lin.linear_f64(z, stream, BITS, IN_DIM, OUT_DIM, svh, strips=strips, threads=threads)
@@ -284,9 +286,9 @@ def cpu_baseline(host_inputs, rows: int) -> dict:
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{rows} fp16 row(s): float64 linear over {sample} of {n_strips} strips "
-                  f"({IN_DIM} x {128 * sample} weights) on {threads} threads, {dt:.1f} s; "
-                  f"rot_in (fp32 steps, 1 thread) timed alone",
+        "sample": f"{rows} fp16 row(s): float64 linear over {sample} of {n_strips} strips, spread evenly "
+                  f"({IN_DIM} x {128 * sample} weights) on {threads} threads, {dt:.1f} s of wall time, "
+                  f"extrapolated to all strips; rot_in (fp32 steps, 1 thread) timed alone",
         "rows_per_s": round(rows / (linear_s + rot_s), 6),
         "linear_s_per_step": round(linear_s, 4),
         "rot_in": {"s_per_step": round(rot_s, 6), "rows_per_s": round(rows / rot_s, 2), "cores": 1},

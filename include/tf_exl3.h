@@ -175,9 +175,10 @@ int tf_exl3_linear_mfma(int bits, int rows, int in_dim, int out_dim, const uint1
  * launch with rot_in's arithmetic unchanged. Every workgroup rotates its pass's rows into LDS with the same arithmetic as
  * tf_exl3_rot_in and then runs tf_exl3_linear's own tile-row walk, so y is bit
  * for bit what tf_exl3_rot_in followed by tf_exl3_linear gives, with one launch
- * and no z buffer. Each workgroup recomputes the rotation of its rows (about 6%
- * more vector work than the linear for one 5120-wide row, which on that shape
- * costs more than the launch it saves). Passes hold as many rows as fit in 48 KiB
+ * and no z buffer. Each workgroup recomputes the rotation of its rows (about 5%
+ * more vector work than the linear for one 5120-wide row: on the LM head about what
+ * the saved launch is worth; on a one-strip layer, whose step is mostly launch
+ * latency, the single launch is the faster route). Passes hold as many rows as fit in 48 KiB
  * of LDS (tf_exl3_project_pass_rows: 2 at in_dim 5120) and each pass streams the
  * weights once, so beyond a pass's rows tf_exl3_rot_in + tf_exl3_linear, which
  * stream them once per 16 rows, are the faster route.

@@ -10,9 +10,12 @@
 // tf_exl3_linear, without the second launch or the round trip of z through HBM.
 //
 // Every workgroup rotates all of its pass's rows (the waves split the 128-blocks),
-// so the rotation is repeated once per strip: for one 5120-wide row about 6% more
-// VALU work than the linear alone, which on the LM head outweighs the launch it
-// saves. The host sizes passes so the rows' z and the partial sums fit in LDS.
+// so the rotation is repeated once per strip: for one 5120-wide row about 5% more
+// VALU work than the linear alone, plus z read from LDS instead of through the
+// scalar cache; on the LM head that costs about what the saved launch does, while
+// on a one-strip layer (the indexer), whose step is mostly launch latency, the
+// single launch takes about 60% of the two launches' time. The host sizes passes so
+// the rows' z and the partial sums fit in LDS.
 #include "exl3_launch.hpp"
 #include "exl3_strip.hpp"
 
