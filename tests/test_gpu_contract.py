@@ -53,13 +53,19 @@ def registrations(bits):
     return regs
 
 
-def oracle_strips(n, seed):
+def oracle_strips(n, seed, count=64):
+    """Every strip for narrow outputs; else `count` strips: the first two, the middle
+    one and the last two, and seeded picks for the rest."""
     m = n // 128
     if m <= 256:
         return None  # every strip
-    picks = {0, 1, m // 2, m - 2, m - 1}
-    picks |= {int(v) for v in synth.splitmix64(seed, 80) % np.uint64(m)}
-    return sorted(picks)[:64]
+    picks = [0, 1, m // 2, m - 2, m - 1]
+    for v in synth.splitmix64(seed, 4 * count) % np.uint64(m):
+        if len(picks) == count:
+            break
+        if int(v) not in picks:
+            picks.append(int(v))
+    return sorted(picks)
 
 
 def five_runs(engine, zt, tt, vt, bits, n, waves, out):

@@ -1,7 +1,7 @@
 """A stream past 2 GiB: 8-bit, 16384 -> 163840 (2.68 GB). Every path on it, checked on
-three sampled strips (the first, one in the middle, the last, whose tiles lie past the
-2 GiB mark) against the oracle's float64 result, and the bit-equal paths against the
-decode linear on every output."""
+64 strips spread evenly from the first to the last (in the tile layout every strip's
+tile rows from 820 on lie past the 2 GiB mark) against the oracle's threaded float64
+result, and the bit-equal paths against the decode linear on every output."""
 
 import numpy as np
 import pytest
@@ -17,7 +17,7 @@ from tests.gpu_util import down, same_bits, say, up
 pytestmark = pytest.mark.gpu
 
 BITS, K, N = 8, 16384, 163840
-STRIPS = [0, 640, 1279]
+STRIPS = [int(v) for v in np.linspace(0, N // 128 - 1, 64).round()]
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +33,7 @@ def large():
 
 
 def check_strips(y, z, stream, svh):
-    y64 = lin.linear_f64(z, stream, BITS, K, N, svh, strips=STRIPS)
+    y64 = lin.linear_f64(z, stream, BITS, K, N, svh, strips=STRIPS, threads=lin.reference_threads())
     err = lin.gate_error(y[:, lin.strip_columns(STRIPS)], "f32", y64)
     assert err <= lin.GATE, err
 
