@@ -47,7 +47,8 @@ enum {
   TF_OK = 0,
   TF_E_BITS = -1,   /* bits not in {2, 3, 4, 5, 6, 8} */
   TF_E_SHAPE = -2,  /* a dimension < 128, not a multiple of 128, or a stream >= 4 GiB */
-  TF_E_ROWS = -3,   /* rows < 0, or more than 1048560 (65535 passes of 16; fewer for project) */
+  TF_E_ROWS = -3,   /* rows < 0, or more than the launch grid holds: 1048560 for the linear (65535
+                       passes of 16), fewer for project, rows * in_dim / 128 below 2^33 for rot_in */
   TF_E_DTYPE = -4,  /* element type outside the table above */
   TF_E_NULL = -5,   /* a required pointer is NULL */
   TF_E_ALIGN = -6,  /* trellis or z not 16-byte aligned, or a row buffer not element-aligned */
@@ -71,7 +72,7 @@ enum {
  *  x      [rows][in_dim], row-major, element type x_dtype (TF_DT_F32/F16/BF16)
  *  suh    [in_dim] fp16 input signs/scales
  *  z      [rows][in_dim] fp16 output, row-major, 16-byte aligned, must not overlap x
- *  rows   >= 0 (0 launches nothing)
+ *  rows   >= 0 (0 launches nothing); rows * in_dim / 128 below 2^33 (TF_E_ROWS)
  *  in_dim multiple of 128
  */
 int tf_exl3_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z,

@@ -145,6 +145,8 @@ def test_rot_in_refusals(lib):
     assert f(FAKE + 2, 0, FAKE + 0x10000, FAKE + 0x20000, 1, 128, None) == -6  # fp32 rows need 4-byte alignment
     assert f(FAKE, 0, FAKE + 0x10000, FAKE + 0x100, 1, 128, None) == -7  # z overlaps x
     assert f(FAKE, 1, FAKE + 0x10000, FAKE + 0x20000, 0, 128, None) == 0
+    # A grid beyond 2^31 workgroups of four 128-blocks is refused, not truncated.
+    assert f(FAKE, 1, FAKE + 0x10000, FAKE + 0x20000, 2**31 - 1, 128 * 8, None) == -3
 
 
 def test_debug_split_refusals(lib):

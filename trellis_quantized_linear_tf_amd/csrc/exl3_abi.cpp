@@ -71,7 +71,8 @@ const char* tf_exl3_status_string(int status) {
     case TF_OK: return "ok";
     case TF_E_BITS: return "bits must be 2, 3, 4, 5, 6 or 8 (widthIndex)";
     case TF_E_SHAPE: return "in_dim and out_dim must be multiples of 128, and the stream under 4 GiB (fits)";
-    case TF_E_ROWS: return "rows must be >= 0 and at most 1048560 (65535 passes of 16 rows)";
+    case TF_E_ROWS:
+      return "rows must be >= 0 and fit the launch grid (at most 1048560 = 65535 passes of 16 rows for the linear)";
     case TF_E_DTYPE: return "element type must be TF_DT_F32, TF_DT_F16 or TF_DT_BF16";
     case TF_E_NULL: return "a required pointer is NULL";
     case TF_E_ALIGN: return "trellis and z must be 16-byte aligned and row buffers element-aligned";
@@ -114,6 +115,8 @@ int tf_exl3_rot_in(const void* x, int x_dtype, const uint16_t* suh, uint16_t* z,
   if (!dtype_ok(x_dtype)) return TF_E_DTYPE;
   if (!dim_ok(in_dim)) return TF_E_SHAPE;
   if (rows < 0) return TF_E_ROWS;
+  // One wave per 128-block, four per workgroup: the grid must stay below 2^31 workgroups.
+  if ((long long)rows * (in_dim / 128) > 4LL * 0x7FFFFFFFLL) return TF_E_ROWS;
   if (rows == 0) return TF_OK;
   if (x == nullptr || suh == nullptr || z == nullptr) return TF_E_NULL;
   if (!aligned(z, 16) || !aligned(x, elem_size(x_dtype)) || !aligned(suh, 2)) return TF_E_ALIGN;
