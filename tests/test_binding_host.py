@@ -118,3 +118,16 @@ def test_refused_shapes_reach_the_library_status():
     """A shape the library refuses (no stream size) is left to its status code."""
     with pytest.raises(ValueError, match="on the GPU"):
         tq.linear(f16(1, 200), stream(16), f16(N), BITS, N)
+
+
+def test_stream_size_rule_matches_the_library():
+    """The binding sizes streams without a library call; its rule must be the library's,
+    refusals (0 there, None here) included."""
+    from trellis_quantized_linear_tf_amd import _lib
+
+    lib = _lib.load()
+    for bits in range(0, 10):
+        for k in (0, 64, 128, 200, 256, 5120, 65536, 131072):
+            for n in (128, 256, 129280, 262144, 1 << 20):
+                want = lib.tf_exl3_trellis_bytes(bits, k, n)
+                assert (_lib._stream_bytes(bits, k, n) or 0) == want, (bits, k, n)

@@ -128,42 +128,48 @@ def _torch():
     return torch
 
 
+# Element types, built once on first use (torch is imported lazily).
+_DTYPES = None
+
+
+def _dtypes():
+    global _DTYPES
+    if _DTYPES is None:
+        torch = _torch()
+        _DTYPES = (
+            (torch.float16, torch.int16),  # fp16 bit patterns (z, suh, svh)
+            (torch.float32, torch.float16, torch.bfloat16),  # rows and outputs
+            {torch.float32: TF_DT_F32, torch.float16: TF_DT_F16, torch.bfloat16: TF_DT_BF16},
+        )
+    return _DTYPES
+
+
 def _dt_code(dtype) -> int:
-    torch = _torch()
-    if dtype == torch.float32:
-        return TF_DT_F32
-    if dtype == torch.float16:
-        return TF_DT_F16
-    if dtype == torch.bfloat16:
-        return TF_DT_BF16
-    raise ValueError(f"unsupported element type {dtype}")
+    code = _dtypes()[2].get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported element type {dtype}")
+    return code
 
 
 def _ptr(t) -> int | None:
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError("tensors must live on the GPU")
-    if not t.is_contiguous():
-        raise ValueError("tensors must be contiguous")
-    return t.data_ptr()
+    """Device address of a tensor that _same_gpu has accepted (None stays NULL)."""
+    return None if t is None else t.data_ptr()
 
 
 # Argument checks. The C ABI sees plain pointers, not buffer sizes, so a short
 # stream or a wrong-shaped output would become an out-of-bounds device access,
 # and an fp32 tensor passed where fp16 bits are read would be misread silently.
 # Every wrapper checks element types, shapes and byte sizes first (these checks
-# need no GPU), then that all tensors are contiguous and on one GPU.
+# need no GPU), then that all tensors are contiguous and on one GPU. They run on
+# every call, so they are kept to attribute reads and comparisons.
 
 
 def _half_bits_dtypes():
-    torch = _torch()
-    return (torch.float16, torch.int16)
+    return _dtypes()[0]
 
 
 def _row_dtypes():
-    torch = _torch()
-    return (torch.float32, torch.float16, torch.bfloat16)
+    return _dtypes()[1]
 
 
 def _nbytes(t) -> int:
@@ -175,9 +181,9 @@ def _need(name: str, t, dtypes=None, shape=None, nbytes=None) -> None:
         raise ValueError(f"{name} is required")
     if dtypes is not None and t.dtype not in dtypes:
         raise ValueError(f"{name} must have element type {' or '.join(map(str, dtypes))}, not {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
-    if nbytes is not None and _nbytes(t) != nbytes:
+    if nbytes is not None and t.numel() * t.element_size() != nbytes:
         raise ValueError(f"{name} must hold {nbytes} bytes, not {_nbytes(t)}")
 
 
@@ -187,26 +193,38 @@ def _need_2d(name: str, t) -> tuple:
     return tuple(t.shape)
 
 
+_WIDTH_SET = frozenset((2, 3, 4, 5, 6, 8))
+
+
 def _stream_bytes(bits: int, in_dim: int, out_dim: int) -> int | None:
-    """Stream size the library expects, or None where the library refuses the shape
-    (it then returns its status before any launch)."""
-    n = trellis_bytes(bits, in_dim, out_dim)
-    return n if n > 0 else None
+    """Stream size the library expects (tf_exl3_trellis_bytes' rule, evaluated here so
+    that a call costs no extra library round trip; a host test checks the two agree),
+    or None where the library refuses the shape (it then returns its status before any
+    launch)."""
+    if bits not in _WIDTH_SET or in_dim < 128 or out_dim < 128 or in_dim % 128 or out_dim % 128:
+        return None
+    n = in_dim * out_dim * bits // 8
+    return n if n < (1 << 32) else None
 
 
 def _same_gpu(*tensors) -> None:
-    ts = [t for t in tensors if t is not None]
-    for t in ts:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-    if len({t.device for t in ts}) > 1:
-        raise ValueError("all tensors must be on one GPU")
+        d = t.get_device()
+        if dev is None:
+            dev = d
+        elif d != dev:
+            raise ValueError("all tensors must be on one GPU")
 
 
 def _stream(t) -> int:
-    return _torch().cuda.current_stream(t.device).cuda_stream
+    return _torch().cuda.current_stream(t.get_device()).cuda_stream
 
 
 def rot_in(x, suh, z=None):
